@@ -1,0 +1,221 @@
+"""Benchmark of the Muon step on the 3.8B GPT matrix set (one MI355X).
+
+A step is one muon_step call over all 168 matrices (momentum, Frobenius
+normalisation, 5 Newton-Schulz steps, weight update), inputs resident in HBM.
+Prints one JSON line:  metric / value (ms per step) / NS TFLOP/s and its
+fraction of the dense bf16 MFMA peak / roofline of the dominant kernel /
+the fp64 oracle timed on the host cores as a CPU baseline.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--compute bf16|fp32]
+"""
+import argparse
+import gc
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"bf16": 2500.0, "fp32": 157.3}   # dense MFMA TFLOP/s, MI355X datasheet
+HBM_PEAK_GBS = 8000.0
+METRIC = "Muon step ms, 3.8B matrix set; NS TFLOP/s and % of bf16 MFMA peak"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="gpt_3.8b_28layers")
+    p.add_argument("--compute", default="bf16", choices=["bf16", "fp32"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-budget", type=float, default=30.0,
+                   help="seconds of oracle work at most for the CPU baseline")
+    return p.parse_args()
+
+
+def kernel_summary(records, steps):
+    """Aggregate the per-launch HIP-event log by (kind, m, n)."""
+    agg = {}
+    for r in records:
+        key = (r["kind"], r["m"], r["n"])
+        a = agg.setdefault(key, {"kind": r["kind"], "m": r["m"], "n": r["n"], "launches": 0,
+                                 "ms": 0.0, "flops": 0.0, "bytes": 0.0, "batch": r["batch"]})
+        a["launches"] += 1
+        a["ms"] += r["ms"]
+        a["flops"] += r["flops"]
+        a["bytes"] += r["bytes"]
+    out = sorted(agg.values(), key=lambda a: -a["ms"])
+    for a in out:
+        a["ms_per_step"] = a["ms"] / steps
+        a["avg_launch_ms"] = a["ms"] / a["launches"]
+        a["tflops"] = a["flops"] / (a["ms"] * 1e-3) / 1e12 if a["ms"] > 0 else 0.0
+        a["gbs"] = a["bytes"] / (a["ms"] * 1e-3) / 1e9 if a["ms"] > 0 else 0.0
+    return out
+
+
+def traffic_from_profiles(kernel_key):
+    """HBM bytes per launch of the dominant kernel from a committed rocprofv3
+    PMC summary, if one exists for the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        import hashlib
+        with open(path) as f:
+            data = json.load(f)
+        src = os.path.join(ROOT, "muon_newton_schulz_step_amd", "csrc", "muon_kernels.hip")
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if data.get("kernel_source_sha256") != digest:
+            return None
+        return data.get("kernels", {}).get(kernel_key)
+    except Exception:
+        return None
+
+
+def cpu_baseline(w, budget_s):
+    """fp64 oracle on a bounded sample: one matrix of every oriented group,
+    extrapolated by the group counts to the full step."""
+    import numpy as np
+    import oracle
+    import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"), default=os.cpu_count())
+    except Exception:
+        threads = os.cpu_count()
+    groups = w.oriented_groups()
+    first = {}
+    for i, (r, c) in enumerate(w.shapes):
+        first.setdefault((min(r, c), max(r, c)), i)
+    order = sorted(groups, key=lambda k: k[0] * k[0] * k[1])
+    total_ms, done, spent = 0.0, [], 0.0
+    for key in order:
+        idx = first[key]
+        x = wl.make_inputs(w, device="cpu", indices=[idx])
+        g = x["grads"][0].double().numpy()
+        b = x["bufs"][0].double().numpy()
+        p = x["params"][0].double().numpy()
+        t0 = time.perf_counter()
+        oracle.muon_step(p, g, b, w.mu, w.lr, x["scales"][0], w.coeff_table)
+        dt = time.perf_counter() - t0
+        spent += dt
+        total_ms += dt * 1e3 * groups[key]
+        done.append(f"{key[0]}x{key[1]}")
+        if spent > budget_s:
+            break
+    complete = len(done) == len(order)
+    return {
+        "value": total_ms if complete else None,
+        "unit": "ms per step (extrapolated)",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"one matrix per oriented group ({', '.join(done)}), fp64 numpy, "
+                   f"x group counts {[groups[k] for k in order]}; {spent:.1f} s of CPU work"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the Muon step shards by whole matrix and "
+              f"this build runs one GPU's share; --gpus {args.gpus} is not supported.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import muon_newton_schulz_step_amd as mn
+    import workloads as wl
+
+    w = wl.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inputs = wl.make_inputs(w, device=dev)
+    torch.cuda.synchronize()
+    ws = mn.Workspace()
+
+    def one_step():
+        mn.step(inputs["params"], inputs["grads"], inputs["bufs"], mu=w.mu, lr=w.lr,
+                scales=inputs["scales"], coeffs=w.coeff_table, compute=args.compute,
+                workspace=ws)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    gc.collect()
+    gc.disable()
+    mn.timing_enable(True)
+    mn.timing_read()  # drop warm-up records
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        one_step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    mn.timing_enable(False)
+    gc.enable()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    records = mn.timing_read()
+    kernels = kernel_summary(records, args.steps)
+    ns = [k for k in kernels if k["kind"] in ("gram", "poly", "update")]
+    ns_ms = sum(k["ms"] for k in ns) / args.steps
+    flops = w.ns_flops_counted()
+    ns_tflops = flops / (ns_ms * 1e-3) / 1e12
+    step_tflops = flops / (ms_per_step * 1e-3) / 1e12
+    dom = kernels[0]
+    dom_key = f"{dom['kind']}_{dom['m']}x{dom['n']}"
+    bound = "mfma" if dom["kind"] in ("gram", "poly", "update") else "hbm"
+    if bound == "mfma":
+        achieved = dom["flops"] / dom["launches"] / (dom["avg_launch_ms"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK[args.compute],
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK[args.compute], 4)}
+    else:
+        achieved = dom["bytes"] / dom["launches"] / (dom["avg_launch_ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof["kernel"] = dom_key
+    roof["avg_launch_ms"] = round(dom["avg_launch_ms"], 4)
+    roof["traffic"] = traffic_from_profiles(dom_key)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_sample_budget)
+
+    groups = w.oriented_groups()
+    out = {
+        "metric": METRIC,
+        "value": round(ms_per_step, 3),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": args.compute,
+        "data": "synthetic (seeded, generated on the GPU)",
+        "config": {"workload": w.name, "matrices": len(w.shapes),
+                   "oriented_groups": {f"{m}x{n}": c for (m, n), c in groups.items()},
+                   "ns_steps": w.n_steps, "coeffs": list(w.coeffs),
+                   "parallelism": "single GPU (one GPU's share of a matrix-sharded step)"},
+        "ns_tflops": round(ns_tflops, 2),
+        "ns_ms_per_step": round(ns_ms, 3),
+        "ns_frac_of_peak": round(ns_tflops / PEAK[args.compute], 4),
+        "step_tflops": round(step_tflops, 2),
+        "counted_ns_tflop_per_step": round(flops / 1e12, 3),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": [{k2: (round(v, 4) if isinstance(v, float) else v) for k2, v in k.items()
+                     if k2 in ("kind", "m", "n", "batch", "launches", "ms_per_step",
+                               "avg_launch_ms", "tflops", "gbs")} for k in kernels],
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

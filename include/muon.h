@@ -1,0 +1,167 @@
+/*
+ * muon.h - C ABI of the MI355X (gfx950) Muon step library, libmuon.so.
+ *
+ * The Muon step for a GPT's 2-D weight matrices, as described by page 1
+ * (web3.cnoyu.systems review of karpathy/autoresearch's train.py, paragraph
+ * on the Muon half of MuonAdamW): Nesterov momentum on the gradient, then a
+ * 5-step Newton-Schulz iteration towards the orthogonal polar factor
+ * (tall: A = X^T X, X <- aX + X(bA + cA^2); wide: A = X X^T,
+ * X <- aX + (bA + cA^2)X; per-step coefficients from a precomputed table),
+ * whose result is the update direction for the weights.  Page 1 also says
+ * the momentum buffer has the parameter's shape and is stacked per shape
+ * group; this library groups the matrices of a call by oriented shape.
+ *
+ * Conventions shared by every entry point:
+ *  - Matrices are dense row-major; "rows x cols" is the parameter's shape.
+ *    The oriented shape is m = min(rows, cols), n = max(rows, cols).
+ *  - Device pointers are caller-owned device memory; host pointers (shape
+ *    arrays, pointer arrays, scales, coefficient tables) are read during the
+ *    call only.  The library allocates no device memory: scratch comes from
+ *    the caller's workspace, sized by the matching *_workspace_bytes query.
+ *  - Work is enqueued on `stream` (0 = the null stream) and is asynchronous:
+ *    results are valid once the caller synchronises that stream.  The
+ *    library never synchronises the device.
+ *  - All argument checks run on the host before anything is enqueued, so a
+ *    call that returns MUON_ERR_INVALID_ARG, MUON_ERR_UNSUPPORTED or
+ *    MUON_ERR_WORKSPACE had no side effect.  MUON_ERR_HIP means a launch
+ *    failed; part of the work may already be enqueued.
+ *  - Non-finite values in the data propagate; they are not checked.
+ *  - Repeated calls on the same inputs give bitwise-identical results (all
+ *    reductions use a fixed order; there are no floating-point atomics).
+ *  - Calls are re-entrant when they use distinct workspaces.
+ */
+#ifndef MUON_H
+#define MUON_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types.  MUON_BF16 is bfloat16 (round-to-nearest-even on every
+ * fp32 -> bf16 conversion), MUON_FP32 is IEEE binary32. */
+typedef enum { MUON_BF16 = 0, MUON_FP32 = 1 } muon_dtype;
+
+/* One row of the Newton-Schulz coefficient table: step k computes
+ * X <- a_k X + (b_k A + c_k A^2) X in the wide form. */
+typedef struct { float a, b, c; } muon_coeff;
+
+typedef enum {
+  MUON_OK = 0,
+  MUON_ERR_INVALID_ARG = -1, /* null pointer, bad size, misalignment, aliasing */
+  MUON_ERR_UNSUPPORTED = -2, /* valid request this build does not implement */
+  MUON_ERR_WORKSPACE = -3,   /* workspace missing, too small or misaligned */
+  MUON_ERR_HIP = -4          /* a HIP launch or runtime call failed */
+} muon_status;
+
+#define MUON_MAX_STEPS 64          /* n_steps must lie in [1, MUON_MAX_STEPS] */
+#define MUON_MAX_ELEMENTS (1LL << 31) /* per matrix, after padding to the tile grid */
+#define MUON_WORKSPACE_ALIGN 256   /* required alignment of `workspace`, bytes */
+#define MUON_PTR_ALIGN 16          /* required alignment of every matrix pointer */
+
+/* ---------------------------------------------------------------- queries */
+
+/* Text for a muon_status value (static storage; never NULL). */
+const char* muon_status_string(int status);
+
+/* Bytes of workspace muon_orthogonalize needs for `batch` matrices of
+ * rows x cols with the given compute precision.  0 for invalid sizes. */
+size_t muon_orthogonalize_workspace_bytes(int batch, int rows, int cols, int compute);
+
+/* Bytes of workspace muon_step needs for the n matrices rows[i] x cols[i].
+ * 0 for invalid sizes or n == 0. */
+size_t muon_step_workspace_bytes(int n, const int* rows, const int* cols, int compute);
+
+/* The grouping muon_step uses (page 1: momentum stacked per shape group).
+ * Matrices are grouped by oriented shape (min(rows,cols), max(rows,cols)),
+ * groups numbered in order of first appearance.  Writes group_of[i] for
+ * i < n and, for g < *n_groups, group_m[g], group_n[g], group_count[g];
+ * the group arrays must hold n entries.  Pure host code; no HIP call. */
+int muon_plan_groups(int n, const int* rows, const int* cols, int* group_of,
+                     int* group_m, int* group_n, int* group_count, int* n_groups);
+
+/* ---------------------------------------------------------- computations */
+
+/* Orthogonalise a batch of same-shape matrices: for each matrix G,
+ *   X_0 = G / (||G||_F + eps);  for k < n_steps:  X_{k+1} = a_k X_k + (b_k A_k + c_k A_k^2) X_k
+ * with A_k = X_k X_k^T (wide or square) and the transposed forms for tall
+ * matrices (page 1, Newton-Schulz paragraph), and writes out = X_{n_steps}.
+ *   in, out       device, `batch` matrices rows x cols, matrix i at
+ *                 element offset i * batch_stride (batch_stride >= rows*cols);
+ *                 out may alias in exactly (same pointer); any other overlap
+ *                 is undefined.
+ *   in_dtype      MUON_BF16 or MUON_FP32; out_dtype likewise.
+ *   coeffs        host, n_steps rows (copied during the call).
+ *   eps           >= 0, finite (the step's default is 1e-7).
+ *   compute       MUON_BF16: bf16 MFMA operands with fp32 accumulation and
+ *                 an fp32 copy of X for the a*X term; MUON_FP32: fp32 throughout.
+ *   workspace     device, >= muon_orthogonalize_workspace_bytes(...) bytes,
+ *                 MUON_WORKSPACE_ALIGN-aligned; contents on entry are ignored.
+ * batch == 0 returns MUON_OK with nothing enqueued. */
+int muon_orthogonalize(const void* in, int in_dtype, void* out, int out_dtype,
+                       int batch, int rows, int cols, long long batch_stride,
+                       const muon_coeff* coeffs, int n_steps, float eps, int compute,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* One Muon step on n matrices of any mix of shapes (page 1: Nesterov
+ * momentum, Newton-Schulz orthogonalisation, the orthogonal factor as the
+ * update direction).  For each matrix i, in place:
+ *   momentum[i] <- mu * momentum[i] + g_i
+ *   u           =  g_i + mu * momentum[i]
+ *   O           =  the muon_orthogonalize result for u
+ *   params[i]   <- params[i] - lr * scale[i] * O
+ *   rows, cols     host arrays of n shapes.
+ *   params         host array of n device pointers, fp32 rows x cols, in/out.
+ *   param_dtype    MUON_FP32 (bf16 parameters return MUON_ERR_UNSUPPORTED).
+ *   grads          host array of n device pointers, read only.
+ *   grad_dtype     MUON_BF16 or MUON_FP32.
+ *   momentum       host array of n device pointers, fp32 rows x cols, in/out.
+ *   scale          host array of n per-matrix multipliers of lr.
+ *   coeffs, n_steps, eps, compute, workspace: as for muon_orthogonalize,
+ *                  with the workspace from muon_step_workspace_bytes.
+ * params[i], grads[i] and momentum[i] must not overlap one another.
+ * n == 0 returns MUON_OK with nothing enqueued. */
+int muon_step(int n, const int* rows, const int* cols,
+              void* const* params, int param_dtype,
+              const void* const* grads, int grad_dtype,
+              float* const* momentum, float mu, float lr, const float* scale,
+              const muon_coeff* coeffs, int n_steps, float eps, int compute,
+              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------ measurement */
+
+/* Kernel classes reported by the timing log. */
+typedef enum {
+  MUON_K_PREP = 0,   /* momentum (or input read), norm partials, oriented X_0 */
+  MUON_K_NORM = 1,   /* per-matrix 1 / (||u||_F + eps) */
+  MUON_K_GRAM = 2,   /* A = X X^T, one triangle, mirrored */
+  MUON_K_POLY = 3,   /* B = b A + c A^2 */
+  MUON_K_UPDATE = 4  /* X <- a X + B X (last step: weight update or output) */
+} muon_kernel_kind;
+
+typedef struct {
+  int kind;        /* muon_kernel_kind */
+  int m, n;        /* oriented shape of the launch's matrices */
+  int batch;       /* matrices in the launch */
+  int step;        /* Newton-Schulz step, -1 for PREP and NORM */
+  float ms;        /* elapsed time between HIP events around the launch */
+  double flops;    /* counted flops: GRAM 2m^2n, POLY 2m^3, UPDATE 2m^2n per matrix */
+  double bytes;    /* algorithmic HBM bytes of the launch (see the design notes) */
+} muon_timing_record;
+
+/* Turn per-launch HIP-event timing on (1) or off (0) for later calls in
+ * this process.  Events are recorded on the call's stream around every
+ * kernel launch.  Returns the previous setting. */
+int muon_timing_enable(int on);
+
+/* Wait for the recorded events, write up to `cap` records (oldest first)
+ * to `out`, set *n_out to the number written, and clear the log.
+ * Returns MUON_OK or MUON_ERR_HIP. */
+int muon_timing_read(muon_timing_record* out, int cap, int* n_out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MUON_H */

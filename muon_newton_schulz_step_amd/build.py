@@ -1,0 +1,64 @@
+"""Build libmuon.so in-tree with hipcc for gfx950.
+
+``python -m muon_newton_schulz_step_amd.build`` or ``build()`` compiles the HIP
+kernels and the host runtime into ``muon_newton_schulz_step_amd/libmuon.so``.
+It always recompiles (a few tens of seconds) and replaces the library
+atomically.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libmuon.so")
+SOURCES = ["muon_kernels.hip", "muon_api.cpp"]
+ARCH = os.environ.get("MUON_OFFLOAD_ARCH", "gfx950")
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libmuon.so)")
+
+
+def compile_command(out: str):
+    return [
+        hipcc(), "-O3", "-std=c++17", "-fPIC", "-shared",
+        f"--offload-arch={ARCH}",
+        # no packed-fp32 instructions anywhere in device code
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wall", "-Wno-unused-function",
+        "-I", INCLUDE, "-I", CSRC,
+        *[os.path.join(CSRC, s) for s in SOURCES],
+        "-o", out,
+    ]
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + f".tmp{os.getpid()}"
+    cmd = compile_command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass does not know the device-only feature; drop that noise
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(l for l in proc.stderr.splitlines() if noise not in l)
+    if proc.returncode != 0:
+        if os.path.exists(tmp):
+            os.remove(tmp)
+        raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{err}")
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

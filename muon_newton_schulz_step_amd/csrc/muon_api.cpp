@@ -1,0 +1,429 @@
+// Host runtime of libmuon.so: argument checks (pure host code, no HIP call,
+// so they run on a machine without a GPU), grouping by oriented shape,
+// workspace layout, launch sequencing and the optional per-launch timing log.
+//
+// Sequence per group of same-oriented-shape matrices (page 1, Muon
+// paragraph: momentum, Newton-Schulz steps, update), on the caller's stream:
+//   prep, norm, then for each step k: gram, poly, update.
+#include <hip/hip_runtime_api.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "muon.h"
+#include "muon_kernels.h"
+
+using namespace muon;
+
+namespace {
+
+constexpr size_t kWsAlign = MUON_WORKSPACE_ALIGN;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+long long pad_dim(long long d) { return (d + kPad - 1) / kPad * kPad; }
+
+bool is_dtype(int d) { return d == MUON_BF16 || d == MUON_FP32; }
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool is_finite(float x) { return std::isfinite(x); }
+
+// Workspace regions for `cnt` matrices of oriented shape m x n.
+struct Layout {
+  int m = 0, n = 0, M = 0, N = 0, cnt = 0, nblk = 0;
+  size_t xf = 0, xb = 0, xt0 = 0, xt1 = 0, A = 0, B = 0, part = 0, inv = 0, total = 0;
+};
+
+bool make_layout(int cnt, int m, int n, bool cbf16, Layout& L) {
+  const long long M = pad_dim(m), N = pad_dim(n);
+  if (M * N > MUON_MAX_ELEMENTS) return false;
+  L.m = m; L.n = n; L.M = (int)M; L.N = (int)N; L.cnt = cnt;
+  L.nblk = (int)((M / kPrepTile) * (N / kPrepTile));
+  const size_t es = cbf16 ? 2 : 4;
+  const size_t MN = (size_t)M * (size_t)N, MM = (size_t)M * (size_t)M;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, kWsAlign);
+    return o;
+  };
+  L.xf = take((size_t)cnt * MN * 4);
+  L.xb = cbf16 ? take((size_t)cnt * MN * 2) : 0;
+  L.xt0 = take((size_t)cnt * MN * es);
+  L.xt1 = take((size_t)cnt * MN * es);
+  L.A = take((size_t)cnt * MM * es);
+  L.B = take((size_t)cnt * MM * es);
+  L.part = take((size_t)cnt * (size_t)L.nblk * 4);
+  L.inv = take((size_t)cnt * 4);
+  L.total = off;
+  return true;
+}
+
+struct Group {
+  int m, n;
+  std::vector<int> idx;
+};
+
+void plan(int n, const int* rows, const int* cols, std::vector<Group>& groups,
+          std::vector<int>* group_of) {
+  groups.clear();
+  if (group_of) group_of->assign(n, -1);
+  for (int i = 0; i < n; ++i) {
+    const int m = rows[i] < cols[i] ? rows[i] : cols[i];
+    const int nn = rows[i] < cols[i] ? cols[i] : rows[i];
+    int g = -1;
+    for (size_t k = 0; k < groups.size(); ++k)
+      if (groups[k].m == m && groups[k].n == nn) { g = (int)k; break; }
+    if (g < 0) {
+      groups.push_back(Group{m, nn, {}});
+      g = (int)groups.size() - 1;
+    }
+    groups[g].idx.push_back(i);
+    if (group_of) (*group_of)[i] = g;
+  }
+}
+
+// ------------------------------------------------------------ timing log
+std::atomic<int> g_timing{0};
+std::mutex g_log_mu;
+struct Pending {
+  muon_timing_record rec;
+  hipEvent_t e0, e1;
+};
+std::vector<Pending> g_log;
+
+template <class F>
+hipError_t timed(int kind, int m, int n, int batch, int step, double flops, double bytes,
+                 hipStream_t s, F&& launch) {
+  if (!g_timing.load(std::memory_order_relaxed)) return launch();
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipError_t err = hipEventCreate(&e0);
+  if (err == hipSuccess) err = hipEventCreate(&e1);
+  if (err == hipSuccess) err = hipEventRecord(e0, s);
+  if (err != hipSuccess) return err;
+  err = launch();
+  const hipError_t err2 = hipEventRecord(e1, s);
+  if (err == hipSuccess) err = err2;
+  muon_timing_record r{kind, m, n, batch, step, 0.f, flops, bytes};
+  std::lock_guard<std::mutex> lk(g_log_mu);
+  g_log.push_back(Pending{r, e0, e1});
+  return err;
+}
+
+// ------------------------------------------------------------ one chunk
+struct Chunk {
+  int cnt;
+  unsigned long long tall_mask;       // bit q: matrix q of the chunk is tall
+  bool momentum;
+  int in_bf16;
+  const void* in; long long s_in;     // orthogonalize input
+  PrepTable pt;                       // step: gradient / momentum pointers
+  float mu;
+  int final_mode;
+  void* out; long long s_out; int out_bf16;
+  WeightTable wt;
+  float neg_lr;
+};
+
+int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeffs, int n_steps,
+              float eps, bool cbf16, hipStream_t s) {
+  const size_t es = cbf16 ? 2 : 4;
+  const long long MN = (long long)L.M * L.N, MM = (long long)L.M * L.M;
+  float* Xf = reinterpret_cast<float*>(ws + L.xf);
+  void* Xb = cbf16 ? static_cast<void*>(ws + L.xb) : nullptr;
+  void* XT[2] = {ws + L.xt0, ws + L.xt1};
+  void* A = ws + L.A;
+  void* B = ws + L.B;
+  float* part = reinterpret_cast<float*>(ws + L.part);
+  float* inv = reinterpret_cast<float*>(ws + L.inv);
+  const double m = L.m, n = L.n, cnt = c.cnt;
+  const double elems = m * n * cnt;
+
+  PrepArgs pa{};
+  pa.m = L.m; pa.n = L.n; pa.M = L.M; pa.N = L.N;
+  pa.tall_mask = c.tall_mask;
+  pa.tiles_n = L.N / kPrepTile;
+  pa.in = c.in; pa.s_in = c.s_in;
+  pa.mu = c.mu;
+  pa.Xf = Xf; pa.sXf = MN;
+  pa.Xb = Xb;
+  pa.XT = XT[0]; pa.sXT = MN;
+  pa.partials = part; pa.nblk = L.nblk;
+  const double gsz = c.in_bf16 ? 2 : 4;
+  const double prep_bytes = elems * (gsz + (c.momentum ? 8.0 : 0.0)) +
+                            cnt * (double)MN * (cbf16 ? 8.0 : 8.0);
+  hipError_t err = timed(MUON_K_PREP, L.m, L.n, c.cnt, -1, 0.0, prep_bytes, s, [&] {
+    return launch_prep(c.in_bf16, cbf16, c.momentum, pa, c.pt, c.cnt, s);
+  });
+  if (err != hipSuccess) return MUON_ERR_HIP;
+  err = timed(MUON_K_NORM, L.m, L.n, c.cnt, -1, 0.0, cnt * L.nblk * 4.0 + cnt * 4.0, s,
+              [&] { return launch_norm(part, L.nblk, eps, inv, c.cnt, s); });
+  if (err != hipSuccess) return MUON_ERR_HIP;
+
+  const int tiles = L.M / 128;
+  for (int k = 0; k < n_steps; ++k) {
+    const bool first = k == 0, last = k == n_steps - 1;
+    GemmArgs g{};
+    g.inv = first ? inv : nullptr;
+    g.a = coeffs[k].a; g.b = coeffs[k].b; g.c = coeffs[k].c;
+    g.m = L.m; g.n = L.n; g.tall_mask = c.tall_mask;
+
+    // A = X X^T (K = N)
+    g.P = cbf16 ? Xb : static_cast<void*>(Xf);
+    g.Q = g.P;
+    g.sP = g.sQ = MN; g.ldp = g.ldq = L.N; g.K = L.N;
+    g.tiles_m = g.tiles_n = tiles; g.tri = 1;
+    g.C = A; g.sC = MM; g.ldc = L.M;
+    err = timed(MUON_K_GRAM, L.m, L.n, c.cnt, k, cnt * 2.0 * m * m * n,
+                cnt * ((double)MN * es + (double)MM * es), s,
+                [&] { return launch_gemm(cbf16, EPI_GRAM, g, c.wt, c.cnt, s); });
+    if (err != hipSuccess) return MUON_ERR_HIP;
+
+    // B = b A + c A A (K = M)
+    g.inv = nullptr;
+    g.P = g.Q = A; g.sP = g.sQ = MM; g.ldp = g.ldq = L.M; g.K = L.M;
+    g.C = B; g.sC = MM; g.ldc = L.M;
+    g.Ain = A; g.sAin = MM;
+    err = timed(MUON_K_POLY, L.m, L.n, c.cnt, k, cnt * 2.0 * m * m * m,
+                cnt * 3.0 * (double)MM * es, s,
+                [&] { return launch_gemm(cbf16, EPI_POLY, g, c.wt, c.cnt, s); });
+    if (err != hipSuccess) return MUON_ERR_HIP;
+
+    // X <- a X + B X  (Q = X^T, K = M)
+    g.inv = first ? inv : nullptr;
+    g.P = B; g.sP = MM; g.ldp = L.M;
+    g.Q = XT[k & 1]; g.sQ = MN; g.ldq = L.M; g.K = L.M;
+    g.tri = 0; g.tiles_m = tiles; g.tiles_n = L.N / 128;
+    g.Xf = Xf; g.sXf = MN; g.ldx = L.N;
+    g.Xb = Xb;
+    g.XTo = XT[(k + 1) & 1]; g.sXT = MN; g.ldxt = L.M;
+    g.last = last;
+    g.final_mode = last ? c.final_mode : FINAL_NONE;
+    g.out = c.out; g.s_out = c.s_out; g.out_bf16 = c.out_bf16;
+    g.neg_lr = c.neg_lr;
+    const double upd_bytes =
+        cnt * ((double)MM * es + (double)MN * es + (double)MN * 4.0) +
+        (last ? (c.final_mode == FINAL_WEIGHTS ? elems * 8.0 : elems * (c.out_bf16 ? 2.0 : 4.0))
+              : cnt * (double)MN * (4.0 + es + (cbf16 ? 2.0 : 0.0)));
+    err = timed(MUON_K_UPDATE, L.m, L.n, c.cnt, k, cnt * 2.0 * m * m * n, upd_bytes, s,
+                [&] { return launch_gemm(cbf16, EPI_UPDATE, g, c.wt, c.cnt, s); });
+    if (err != hipSuccess) return MUON_ERR_HIP;
+  }
+  return MUON_OK;
+}
+
+int check_coeffs(const muon_coeff* coeffs, int n_steps, float eps) {
+  if (!coeffs || n_steps < 1 || n_steps > MUON_MAX_STEPS) return MUON_ERR_INVALID_ARG;
+  for (int k = 0; k < n_steps; ++k)
+    if (!is_finite(coeffs[k].a) || !is_finite(coeffs[k].b) || !is_finite(coeffs[k].c))
+      return MUON_ERR_INVALID_ARG;
+  if (!is_finite(eps) || eps < 0.f) return MUON_ERR_INVALID_ARG;
+  return MUON_OK;
+}
+
+bool shape_ok(int rows, int cols) {
+  if (rows < 1 || cols < 1) return false;
+  return pad_dim(rows) * pad_dim(cols) <= MUON_MAX_ELEMENTS;
+}
+
+bool overlap(const void* p, size_t pb, const void* q, size_t qb) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+  return a < b + qb && b < a + pb;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* muon_status_string(int status) {
+  switch (status) {
+    case MUON_OK: return "MUON_OK: success";
+    case MUON_ERR_INVALID_ARG: return "MUON_ERR_INVALID_ARG: invalid argument";
+    case MUON_ERR_UNSUPPORTED: return "MUON_ERR_UNSUPPORTED: unsupported request";
+    case MUON_ERR_WORKSPACE: return "MUON_ERR_WORKSPACE: workspace missing, too small or misaligned";
+    case MUON_ERR_HIP: return "MUON_ERR_HIP: HIP launch or runtime error";
+    default: return "unknown muon status";
+  }
+}
+
+size_t muon_orthogonalize_workspace_bytes(int batch, int rows, int cols, int compute) {
+  if (batch < 1 || !shape_ok(rows, cols) || !is_dtype(compute)) return 0;
+  Layout L;
+  const int cnt = batch < kChunk ? batch : kChunk;
+  const int m = rows < cols ? rows : cols, n = rows < cols ? cols : rows;
+  if (!make_layout(cnt, m, n, compute == MUON_BF16, L)) return 0;
+  return L.total;
+}
+
+size_t muon_step_workspace_bytes(int n, const int* rows, const int* cols, int compute) {
+  if (n < 1 || !rows || !cols || !is_dtype(compute)) return 0;
+  for (int i = 0; i < n; ++i)
+    if (!shape_ok(rows[i], cols[i])) return 0;
+  std::vector<Group> groups;
+  plan(n, rows, cols, groups, nullptr);
+  size_t best = 0;
+  for (const Group& g : groups) {
+    const int cnt = (int)g.idx.size() < kChunk ? (int)g.idx.size() : kChunk;
+    Layout L;
+    if (!make_layout(cnt, g.m, g.n, compute == MUON_BF16, L)) return 0;
+    if (L.total > best) best = L.total;
+  }
+  return best;
+}
+
+int muon_plan_groups(int n, const int* rows, const int* cols, int* group_of, int* group_m,
+                     int* group_n, int* group_count, int* n_groups) {
+  if (n < 0 || !n_groups) return MUON_ERR_INVALID_ARG;
+  if (n > 0 && (!rows || !cols || !group_of || !group_m || !group_n || !group_count))
+    return MUON_ERR_INVALID_ARG;
+  for (int i = 0; i < n; ++i)
+    if (rows[i] < 1 || cols[i] < 1) return MUON_ERR_INVALID_ARG;
+  std::vector<Group> groups;
+  std::vector<int> gof;
+  plan(n, rows, cols, groups, &gof);
+  for (int i = 0; i < n; ++i) group_of[i] = gof[i];
+  for (size_t g = 0; g < groups.size(); ++g) {
+    group_m[g] = groups[g].m;
+    group_n[g] = groups[g].n;
+    group_count[g] = (int)groups[g].idx.size();
+  }
+  *n_groups = (int)groups.size();
+  return MUON_OK;
+}
+
+int muon_orthogonalize(const void* in, int in_dtype, void* out, int out_dtype, int batch,
+                       int rows, int cols, long long batch_stride, const muon_coeff* coeffs,
+                       int n_steps, float eps, int compute, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  if (batch < 0) return MUON_ERR_INVALID_ARG;
+  if (!is_dtype(in_dtype) || !is_dtype(out_dtype) || !is_dtype(compute))
+    return MUON_ERR_INVALID_ARG;
+  if (int st = check_coeffs(coeffs, n_steps, eps)) return st;
+  if (batch == 0) return MUON_OK;
+  if (!in || !out) return MUON_ERR_INVALID_ARG;
+  if (!shape_ok(rows, cols)) return MUON_ERR_INVALID_ARG;
+  if (batch_stride < (long long)rows * cols) return MUON_ERR_INVALID_ARG;
+  if (!aligned(in, MUON_PTR_ALIGN) || !aligned(out, MUON_PTR_ALIGN)) return MUON_ERR_INVALID_ARG;
+  const size_t need = muon_orthogonalize_workspace_bytes(batch, rows, cols, compute);
+  if (need == 0) return MUON_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < need || !aligned(workspace, kWsAlign))
+    return MUON_ERR_WORKSPACE;
+  const size_t isz = in_dtype == MUON_BF16 ? 2 : 4, osz = out_dtype == MUON_BF16 ? 2 : 4;
+  const size_t span_in = ((size_t)(batch - 1) * batch_stride + (size_t)rows * cols) * isz;
+  const size_t span_out = ((size_t)(batch - 1) * batch_stride + (size_t)rows * cols) * osz;
+  if (in != out && overlap(in, span_in, out, span_out)) return MUON_ERR_INVALID_ARG;
+  if (overlap(workspace, need, in, span_in) || overlap(workspace, need, out, span_out))
+    return MUON_ERR_INVALID_ARG;
+
+  const bool cbf16 = compute == MUON_BF16;
+  const int m = rows < cols ? rows : cols, n = rows < cols ? cols : rows;
+  char* ws = static_cast<char*>(workspace);
+  for (int b0 = 0; b0 < batch; b0 += kChunk) {
+    const int cnt = batch - b0 < kChunk ? batch - b0 : kChunk;
+    Layout L;
+    make_layout(cnt, m, n, cbf16, L);
+    Chunk c{};
+    c.cnt = cnt;
+    c.tall_mask = rows > cols ? (cnt == 64 ? ~0ull : ((1ull << cnt) - 1)) : 0ull;
+    c.momentum = false;
+    c.in_bf16 = in_dtype == MUON_BF16;
+    c.in = static_cast<const char*>(in) + (size_t)b0 * batch_stride * isz;
+    c.s_in = batch_stride;
+    c.final_mode = FINAL_OUT;
+    c.out = static_cast<char*>(out) + (size_t)b0 * batch_stride * osz;
+    c.s_out = batch_stride;
+    c.out_bf16 = out_dtype == MUON_BF16;
+    if (int st = run_chunk(c, L, ws, coeffs, n_steps, eps, cbf16, stream)) return st;
+  }
+  return MUON_OK;
+}
+
+int muon_step(int n, const int* rows, const int* cols, void* const* params, int param_dtype,
+              const void* const* grads, int grad_dtype, float* const* momentum, float mu,
+              float lr, const float* scale, const muon_coeff* coeffs, int n_steps, float eps,
+              int compute, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (n < 0) return MUON_ERR_INVALID_ARG;
+  if (!is_dtype(param_dtype) || !is_dtype(grad_dtype) || !is_dtype(compute))
+    return MUON_ERR_INVALID_ARG;
+  if (int st = check_coeffs(coeffs, n_steps, eps)) return st;
+  if (!is_finite(mu) || !is_finite(lr)) return MUON_ERR_INVALID_ARG;
+  if (n == 0) return MUON_OK;
+  if (!rows || !cols || !params || !grads || !momentum || !scale) return MUON_ERR_INVALID_ARG;
+  const size_t gsz = grad_dtype == MUON_BF16 ? 2 : 4;
+  for (int i = 0; i < n; ++i) {
+    if (!shape_ok(rows[i], cols[i])) return MUON_ERR_INVALID_ARG;
+    if (!params[i] || !grads[i] || !momentum[i]) return MUON_ERR_INVALID_ARG;
+    if (!aligned(params[i], MUON_PTR_ALIGN) || !aligned(grads[i], MUON_PTR_ALIGN) ||
+        !aligned(momentum[i], MUON_PTR_ALIGN))
+      return MUON_ERR_INVALID_ARG;
+    if (!is_finite(scale[i])) return MUON_ERR_INVALID_ARG;
+    const size_t el = (size_t)rows[i] * cols[i];
+    if (overlap(params[i], el * 4, grads[i], el * gsz) ||
+        overlap(params[i], el * 4, momentum[i], el * 4) ||
+        overlap(grads[i], el * gsz, momentum[i], el * 4))
+      return MUON_ERR_INVALID_ARG;
+  }
+  if (param_dtype != MUON_FP32) return MUON_ERR_UNSUPPORTED;
+  const size_t need = muon_step_workspace_bytes(n, rows, cols, compute);
+  if (need == 0) return MUON_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < need || !aligned(workspace, kWsAlign))
+    return MUON_ERR_WORKSPACE;
+
+  const bool cbf16 = compute == MUON_BF16;
+  std::vector<Group> groups;
+  plan(n, rows, cols, groups, nullptr);
+  char* ws = static_cast<char*>(workspace);
+  for (const Group& g : groups) {
+    const int total = (int)g.idx.size();
+    for (int b0 = 0; b0 < total; b0 += kChunk) {
+      const int cnt = total - b0 < kChunk ? total - b0 : kChunk;
+      // Tall and wide matrices of one oriented shape share the launch: the
+      // kernels read each matrix's orientation from the mask.
+      Chunk c{};
+      for (int q = 0; q < cnt; ++q) {
+        const int i = g.idx[b0 + q];
+        c.pt.g[q] = grads[i];
+        c.pt.buf[q] = momentum[i];
+        c.wt.w[q] = static_cast<float*>(params[i]);
+        c.wt.scale[q] = scale[i];
+        if (rows[i] > cols[i]) c.tall_mask |= 1ull << q;
+      }
+      Layout L;
+      make_layout(cnt, g.m, g.n, cbf16, L);
+      c.cnt = cnt;
+      c.momentum = true;
+      c.in_bf16 = grad_dtype == MUON_BF16;
+      c.mu = mu;
+      c.final_mode = FINAL_WEIGHTS;
+      c.neg_lr = -lr;
+      if (int st = run_chunk(c, L, ws, coeffs, n_steps, eps, cbf16, stream)) return st;
+    }
+  }
+  return MUON_OK;
+}
+
+int muon_timing_enable(int on) { return g_timing.exchange(on ? 1 : 0); }
+
+int muon_timing_read(muon_timing_record* out, int cap, int* n_out) {
+  std::vector<Pending> log;
+  {
+    std::lock_guard<std::mutex> lk(g_log_mu);
+    log.swap(g_log);
+  }
+  int st = MUON_OK, w = 0;
+  for (Pending& p : log) {
+    float ms = 0.f;
+    if (hipEventSynchronize(p.e1) != hipSuccess || hipEventElapsedTime(&ms, p.e0, p.e1) != hipSuccess)
+      st = MUON_ERR_HIP;
+    p.rec.ms = ms;
+    if (out && w < cap) out[w++] = p.rec;
+    (void)hipEventDestroy(p.e0);
+    (void)hipEventDestroy(p.e1);
+  }
+  if (n_out) *n_out = w;
+  return st;
+}
+
+}  // extern "C"

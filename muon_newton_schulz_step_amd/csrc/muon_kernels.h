@@ -1,0 +1,82 @@
+// Internal interface between the host runtime (muon_api.cpp) and the HIP
+// kernels (muon_kernels.hip).  Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+namespace muon {
+
+// Matrices handled by one launch when the launch needs per-matrix pointers.
+constexpr int kChunk = 64;
+// Every workspace matrix is padded with zeros to a multiple of kPad in both
+// dimensions, so the GEMM kernels never test bounds.
+constexpr int kPad = 128;
+// Tile of the elementwise prep kernel (oriented coordinates).
+constexpr int kPrepTile = 64;
+
+enum Epi { EPI_GRAM = 0, EPI_POLY = 1, EPI_UPDATE = 2 };
+enum Final { FINAL_NONE = 0, FINAL_OUT = 1, FINAL_WEIGHTS = 2 };
+
+// Inputs of the prep kernel: momentum (step) or plain input (orthogonalize),
+// Frobenius partial sums, and the oriented, zero-padded X_0 copies.
+struct PrepArgs {
+  int m, n, M, N;          // oriented shape and its padded size
+  unsigned long long tall_mask;  // bit i: matrix i is tall (rows = n, cols = m),
+                                 // its oriented X is the original transposed
+  int tiles_n;             // N / kPrepTile
+  const void* in;          // orthogonalize: input base (matrix i at in + i*s_in)
+  long long s_in;
+  float mu;
+  float* Xf;               // fp32 X_0, M x N per matrix
+  long long sXf;
+  void* Xb;                // bf16 X_0, M x N (bf16 compute only)
+  void* XT;                // X_0^T, N x M, compute type
+  long long sXT;
+  float* partials;         // [matrix][tile] sum of u^2
+  int nblk;                // tiles per matrix
+};
+
+struct PrepTable {         // step only: per-matrix gradient / momentum pointers
+  const void* g[kChunk];
+  float* buf[kChunk];
+};
+
+// C[i][j] = sum_k P[i][k] Q[j][k] over a padded batch, with an epilogue.
+struct GemmArgs {
+  const void* P; const void* Q;
+  long long sP, sQ;        // per-matrix strides, elements
+  int ldp, ldq, K;
+  int tiles_m, tiles_n;
+  int tri;                 // 1: lower-triangle tiles only (GRAM, POLY)
+  const float* inv;        // first step: 1/(||u||_F+eps) per matrix, else null
+  float a, b, c;           // step coefficients
+  // GRAM / POLY output (M x M), POLY input A
+  void* C; long long sC; int ldc;
+  const void* Ain; long long sAin;
+  // UPDATE
+  float* Xf; long long sXf; int ldx;     // fp32 X, read a*X, write X_{k+1}
+  void* Xb;                              // bf16 X copy (bf16 compute)
+  void* XTo; long long sXT; int ldxt;    // X_{k+1}^T for the next step
+  int last;                              // last step: final output instead of X
+  int m, n;
+  unsigned long long tall_mask;          // bit i: matrix i is stored tall
+  int final_mode;
+  void* out; long long s_out; int out_bf16;
+  float neg_lr;
+};
+
+struct WeightTable {       // FINAL_WEIGHTS only
+  float* w[kChunk];
+  float scale[kChunk];
+};
+
+// Launchers (return hipGetLastError() of the launch).
+hipError_t launch_prep(int grad_bf16, int compute_bf16, int momentum,
+                       const PrepArgs& a, const PrepTable& t, int batch,
+                       hipStream_t s);
+hipError_t launch_norm(const float* partials, int nblk, float eps, float* inv,
+                       int batch, hipStream_t s);
+hipError_t launch_gemm(int compute_bf16, int epi, const GemmArgs& a,
+                       const WeightTable& t, int batch, hipStream_t s);
+
+}  // namespace muon

@@ -1,0 +1,158 @@
+"""C ABI checks that need no GPU: symbols, argument validation, workspace
+sizing and the grouping planner.  Every rejected call returns before any HIP
+call is made, so these run on a machine without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import muon_newton_schulz_step_amd as mn
+from muon_newton_schulz_step_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+Q = [(3.4445, -4.7750, 2.0315)] * 5
+FAKE = 0x10000  # 16- and 256-byte aligned; never dereferenced by rejected calls
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "muon.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(muon_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = mn.lib()
+    declared = header_functions()
+    assert set(declared) == set(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for st in (0, -1, -2, -3, -4):
+        assert mn.status_string(st).startswith("MUON_")
+    assert "unknown" in mn.status_string(7)
+
+
+def orth(in_ptr=FAKE, in_dtype=0, out_ptr=FAKE * 2, out_dtype=1, batch=1, rows=8, cols=16,
+         stride=None, coeffs=Q, n_steps=None, eps=1e-7, compute=0, ws=FAKE * 1024,
+         ws_bytes=None):
+    lib = mn.lib()
+    if stride is None:
+        stride = rows * cols
+    if n_steps is None:
+        n_steps = len(coeffs)
+    if ws_bytes is None:
+        ws_bytes = lib.muon_orthogonalize_workspace_bytes(max(batch, 1), rows, cols, compute)
+    table = _lib.coeff_array(coeffs) if coeffs is not None else None
+    return lib.muon_orthogonalize(
+        ctypes.c_void_p(in_ptr), in_dtype, ctypes.c_void_p(out_ptr), out_dtype, batch, rows,
+        cols, stride, table, n_steps, eps, compute, ctypes.c_void_p(ws), ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(batch=-1), mn.MUON_ERR_INVALID_ARG),
+    (dict(batch=0), mn.MUON_OK),                       # nothing enqueued
+    (dict(in_ptr=0), mn.MUON_ERR_INVALID_ARG),
+    (dict(out_ptr=0), mn.MUON_ERR_INVALID_ARG),
+    (dict(rows=0), mn.MUON_ERR_INVALID_ARG),
+    (dict(cols=-3), mn.MUON_ERR_INVALID_ARG),
+    (dict(in_dtype=5), mn.MUON_ERR_INVALID_ARG),
+    (dict(out_dtype=-1), mn.MUON_ERR_INVALID_ARG),
+    (dict(compute=2), mn.MUON_ERR_INVALID_ARG),
+    (dict(n_steps=0), mn.MUON_ERR_INVALID_ARG),
+    (dict(coeffs=Q * 13, n_steps=65), mn.MUON_ERR_INVALID_ARG),
+    (dict(coeffs=None, n_steps=5), mn.MUON_ERR_INVALID_ARG),
+    (dict(coeffs=[(float("nan"), 0.0, 0.0)]), mn.MUON_ERR_INVALID_ARG),
+    (dict(eps=-1.0), mn.MUON_ERR_INVALID_ARG),
+    (dict(eps=float("inf")), mn.MUON_ERR_INVALID_ARG),
+    (dict(stride=8 * 16 - 1), mn.MUON_ERR_INVALID_ARG),
+    (dict(in_ptr=FAKE + 2), mn.MUON_ERR_INVALID_ARG),   # misaligned
+    (dict(out_ptr=FAKE + 8), mn.MUON_ERR_INVALID_ARG),  # overlaps input, not equal
+    (dict(rows=1 << 16, cols=1 << 16), mn.MUON_ERR_INVALID_ARG),  # too many elements
+    (dict(ws=0), mn.MUON_ERR_WORKSPACE),
+    (dict(ws_bytes=1024), mn.MUON_ERR_WORKSPACE),
+    (dict(ws=FAKE * 1024 + 16), mn.MUON_ERR_WORKSPACE),  # workspace misaligned
+    (dict(ws=FAKE), mn.MUON_ERR_INVALID_ARG),            # workspace overlaps input
+])
+def test_orthogonalize_rejects_before_enqueue(kw, expect):
+    assert orth(**kw) == expect
+
+
+def step_call(n=2, rows=(8, 16), cols=(16, 8), params=None, grads=None, bufs=None,
+              param_dtype=1, grad_dtype=0, mu=0.95, lr=0.02, scales=(1.0, 1.0), coeffs=Q,
+              n_steps=None, eps=1e-7, compute=0, ws=FAKE * 4096, ws_bytes=None):
+    lib = mn.lib()
+    params = params if params is not None else [FAKE * (i + 1) * 64 for i in range(n)]
+    grads = grads if grads is not None else [FAKE * (i + 1) * 64 + 4096 for i in range(n)]
+    bufs = bufs if bufs is not None else [FAKE * (i + 1) * 64 + 8192 for i in range(n)]
+    r, c = _lib.int_array(rows), _lib.int_array(cols)
+    if ws_bytes is None:
+        ws_bytes = lib.muon_step_workspace_bytes(n, r, c, compute) if n > 0 else 0
+    if n_steps is None:
+        n_steps = len(coeffs)
+    return lib.muon_step(
+        n, r, c, _lib.ptr_array(params), param_dtype, _lib.ptr_array(grads), grad_dtype,
+        _lib.ptr_array(bufs), mu, lr, _lib.float_array(scales), _lib.coeff_array(coeffs),
+        n_steps, eps, compute, ctypes.c_void_p(ws), ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(n=-1), mn.MUON_ERR_INVALID_ARG),
+    (dict(n=0), mn.MUON_OK),
+    (dict(rows=(8, 0)), mn.MUON_ERR_INVALID_ARG),
+    (dict(params=[FAKE * 64, 0]), mn.MUON_ERR_INVALID_ARG),
+    (dict(grads=[FAKE * 64 + 4096, FAKE * 128 + 4098]), mn.MUON_ERR_INVALID_ARG),
+    (dict(bufs=[FAKE * 64, FAKE * 128 + 8192]), mn.MUON_ERR_INVALID_ARG),  # buf aliases param
+    (dict(param_dtype=0), mn.MUON_ERR_UNSUPPORTED),
+    (dict(grad_dtype=3), mn.MUON_ERR_INVALID_ARG),
+    (dict(mu=float("nan")), mn.MUON_ERR_INVALID_ARG),
+    (dict(lr=float("inf")), mn.MUON_ERR_INVALID_ARG),
+    (dict(scales=(1.0, float("nan"))), mn.MUON_ERR_INVALID_ARG),
+    (dict(n_steps=65, coeffs=Q * 13), mn.MUON_ERR_INVALID_ARG),
+    (dict(ws=0), mn.MUON_ERR_WORKSPACE),
+    (dict(ws_bytes=100), mn.MUON_ERR_WORKSPACE),
+])
+def test_step_rejects_before_enqueue(kw, expect):
+    assert step_call(**kw) == expect
+
+
+def test_workspace_sizes():
+    lib = mn.lib()
+    small = lib.muon_orthogonalize_workspace_bytes(1, 256, 128, 0)
+    assert small > 0 and small % 256 == 0
+    # transposed shapes share the oriented layout
+    assert small == lib.muon_orthogonalize_workspace_bytes(1, 128, 256, 0)
+    # fp32 compute needs more than bf16
+    assert lib.muon_orthogonalize_workspace_bytes(1, 256, 128, 1) > small
+    # batches are processed in chunks of at most 64 matrices
+    assert (lib.muon_orthogonalize_workspace_bytes(200, 256, 128, 0)
+            == lib.muon_orthogonalize_workspace_bytes(64, 256, 128, 0))
+    assert lib.muon_orthogonalize_workspace_bytes(0, 256, 128, 0) == 0
+    assert lib.muon_orthogonalize_workspace_bytes(1, 0, 128, 0) == 0
+    # 3.8B matrix set: the largest group is 56 x (3072, 12288)
+    shapes = [(3072, 3072), (1024, 3072), (1024, 3072), (3072, 3072),
+              (12288, 3072), (3072, 12288)] * 28
+    ws = mn.step_workspace_bytes(shapes)
+    assert ws == lib.muon_orthogonalize_workspace_bytes(56, 3072, 12288, 0)
+    assert 15e9 < ws < 25e9
+
+
+def test_plan_groups_by_oriented_shape():
+    shapes = [(768, 768), (768, 3072), (3072, 768), (768, 768), (5, 3), (3, 5), (4, 4)]
+    gof, groups = mn.plan_groups(shapes)
+    assert gof == [0, 1, 1, 0, 2, 2, 3]
+    assert groups == [(768, 768, 2), (768, 3072, 2), (3, 5, 2), (4, 4, 1)]
+    gof, groups = mn.plan_groups([])
+    assert gof == [] and groups == []
+    shapes = [(3072, 3072), (1024, 3072), (1024, 3072), (3072, 3072),
+              (12288, 3072), (3072, 12288)] * 28
+    _, groups = mn.plan_groups(shapes)
+    assert groups == [(3072, 3072, 56), (1024, 3072, 56), (3072, 12288, 56)]
+
+
+def test_timing_log_empty_without_launches():
+    prev = mn.timing_enable(True)
+    assert mn.timing_read() == []
+    mn.timing_enable(prev)
