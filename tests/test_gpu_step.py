@@ -33,7 +33,7 @@ def check_matrix(w, inputs, k, before, bufs_before, compute, coeffs=None):
     dw_err = oracle.relative_frobenius_error(to64(inputs["params"][k]) - before[k],
                                              new_w - before[k])
     assert buf_err <= BUF_TOL, (k, buf_err)
-    assert dw_err <= tol(compute), (k, dw_err)
+    assert dw_err <= tol(compute, w.shapes[k]), (k, dw_err)
     return dw_err
 
 
