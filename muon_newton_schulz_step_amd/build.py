@@ -36,6 +36,7 @@ def compile_command(out: str):
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wall", "-Wno-unused-function",
         "-I", INCLUDE, "-I", CSRC,
+        "-Wl,--no-undefined",
         *[os.path.join(CSRC, s) for s in SOURCES],
         "-o", out,
     ]

@@ -10,6 +10,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -29,6 +30,32 @@ long long pad_dim(long long d) { return (d + kPad - 1) / kPad * kPad; }
 bool is_dtype(int d) { return d == MUON_BF16 || d == MUON_FP32; }
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 bool is_finite(float x) { return std::isfinite(x); }
+
+// MUON_GEMM_TILE=128|256 forces the bf16 GEMM tile (a tuning knob).
+int tile_pref() {
+  static const int v = [] {
+    const char* e = std::getenv("MUON_GEMM_TILE");
+    return e ? std::atoi(e) : 0;
+  }();
+  return v;
+}
+
+// MUON_GROUP_M=<n> sets the tile rows per scheduling group of full grids.
+int group_m() {
+  static const int v = [] {
+    const char* e = std::getenv("MUON_GROUP_M");
+    const int g = e ? std::atoi(e) : 4;
+    return g >= 1 ? g : 4;
+  }();
+  return v;
+}
+
+// 256 x 256 tiles unless that leaves fewer than two blocks per CU.
+int pick_tile(bool cbf16, long long tiles_at_256, int batch) {
+  const int pref = tile_pref();
+  if (pref == 128 || pref == 256) return gemm_tile(cbf16, pref);
+  return gemm_tile(cbf16, tiles_at_256 * batch >= 512 ? 256 : 128);
+}
 
 // Workspace regions for `cnt` matrices of oriented shape m x n.
 struct Layout {
@@ -162,7 +189,9 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
               [&] { return launch_norm(part, L.nblk, eps, inv, c.cnt, s); });
   if (err != hipSuccess) return MUON_ERR_HIP;
 
-  const int tiles = L.M / 128;
+  const int t256 = L.M / 256;
+  const int tile_sym = pick_tile(cbf16, (long long)t256 * (t256 + 1) / 2, c.cnt);
+  const int tile_upd = pick_tile(cbf16, (long long)t256 * (L.N / 256), c.cnt);
   for (int k = 0; k < n_steps; ++k) {
     const bool first = k == 0, last = k == n_steps - 1;
     GemmArgs g{};
@@ -174,11 +203,11 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
     g.P = cbf16 ? Xb : static_cast<void*>(Xf);
     g.Q = g.P;
     g.sP = g.sQ = MN; g.ldp = g.ldq = L.N; g.K = L.N;
-    g.tiles_m = g.tiles_n = tiles; g.tri = 1;
+    g.tiles_m = g.tiles_n = L.M / tile_sym; g.tri = 1;
     g.C = A; g.sC = MM; g.ldc = L.M;
     err = timed(MUON_K_GRAM, L.m, L.n, c.cnt, k, cnt * 2.0 * m * m * n,
                 cnt * ((double)MN * es + (double)MM * es), s,
-                [&] { return launch_gemm(cbf16, EPI_GRAM, g, c.wt, c.cnt, s); });
+                [&] { return launch_gemm(cbf16, EPI_GRAM, tile_sym, g, c.wt, c.cnt, s); });
     if (err != hipSuccess) return MUON_ERR_HIP;
 
     // B = b A + c A A (K = M)
@@ -188,19 +217,19 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
     g.Ain = A; g.sAin = MM;
     err = timed(MUON_K_POLY, L.m, L.n, c.cnt, k, cnt * 2.0 * m * m * m,
                 cnt * 3.0 * (double)MM * es, s,
-                [&] { return launch_gemm(cbf16, EPI_POLY, g, c.wt, c.cnt, s); });
+                [&] { return launch_gemm(cbf16, EPI_POLY, tile_sym, g, c.wt, c.cnt, s); });
     if (err != hipSuccess) return MUON_ERR_HIP;
 
     // X <- a X + B X  (Q = X^T, K = M)
     g.inv = first ? inv : nullptr;
     g.P = B; g.sP = MM; g.ldp = L.M;
     g.Q = XT[k & 1]; g.sQ = MN; g.ldq = L.M; g.K = L.M;
-    g.tri = 0; g.tiles_m = tiles; g.tiles_n = L.N / 128;
+    g.tri = 0; g.tiles_m = L.M / tile_upd; g.tiles_n = L.N / tile_upd;
     g.Xf = Xf; g.sXf = MN; g.ldx = L.N;
     g.Xb = Xb;
     g.XTo = XT[(k + 1) & 1]; g.sXT = MN; g.ldxt = L.M;
-    g.last = last;
     g.final_mode = last ? c.final_mode : FINAL_NONE;
+    g.group_m = group_m();
     g.out = c.out; g.s_out = c.s_out; g.out_bf16 = c.out_bf16;
     g.neg_lr = c.neg_lr;
     const double upd_bytes =
@@ -208,7 +237,10 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
         (last ? (c.final_mode == FINAL_WEIGHTS ? elems * 8.0 : elems * (c.out_bf16 ? 2.0 : 4.0))
               : cnt * (double)MN * (4.0 + es + (cbf16 ? 2.0 : 0.0)));
     err = timed(MUON_K_UPDATE, L.m, L.n, c.cnt, k, cnt * 2.0 * m * m * n, upd_bytes, s,
-                [&] { return launch_gemm(cbf16, EPI_UPDATE, g, c.wt, c.cnt, s); });
+                [&] { return launch_gemm(cbf16, !last ? EPI_UPDATE
+                                             : c.final_mode == FINAL_WEIGHTS ? EPI_FINAL_W
+                                                                             : EPI_FINAL_OUT,
+                                     tile_upd, g, c.wt, c.cnt, s); });
     if (err != hipSuccess) return MUON_ERR_HIP;
   }
   return MUON_OK;

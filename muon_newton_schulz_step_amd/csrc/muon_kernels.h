@@ -10,11 +10,15 @@ namespace muon {
 constexpr int kChunk = 64;
 // Every workspace matrix is padded with zeros to a multiple of kPad in both
 // dimensions, so the GEMM kernels never test bounds.
-constexpr int kPad = 128;
+constexpr int kPad = 256;
 // Tile of the elementwise prep kernel (oriented coordinates).
 constexpr int kPrepTile = 64;
 
-enum Epi { EPI_GRAM = 0, EPI_POLY = 1, EPI_UPDATE = 2 };
+// GEMM epilogues: GRAM A = inv^2 X X^T; POLY B = b A + c A A; UPDATE
+// X <- scl (a X + B X) with X, bf16 X and X^T written; FINAL_W the same
+// value subtracted (times lr * scale) from the weights; FINAL_OUT the same
+// value written to the caller's output.
+enum Epi { EPI_GRAM = 0, EPI_POLY = 1, EPI_UPDATE = 2, EPI_FINAL_W = 3, EPI_FINAL_OUT = 4 };
 enum Final { FINAL_NONE = 0, FINAL_OUT = 1, FINAL_WEIGHTS = 2 };
 
 // Inputs of the prep kernel: momentum (step) or plain input (orthogonalize),
@@ -47,6 +51,8 @@ struct GemmArgs {
   long long sP, sQ;        // per-matrix strides, elements
   int ldp, ldq, K;
   int tiles_m, tiles_n;
+  int tiles_per_mat;       // set by launch_gemm
+  int group_m;             // full grids: tile rows per scheduling group
   int tri;                 // 1: lower-triangle tiles only (GRAM, POLY)
   const float* inv;        // first step: 1/(||u||_F+eps) per matrix, else null
   float a, b, c;           // step coefficients
@@ -57,7 +63,6 @@ struct GemmArgs {
   float* Xf; long long sXf; int ldx;     // fp32 X, read a*X, write X_{k+1}
   void* Xb;                              // bf16 X copy (bf16 compute)
   void* XTo; long long sXT; int ldxt;    // X_{k+1}^T for the next step
-  int last;                              // last step: final output instead of X
   int m, n;
   unsigned long long tall_mask;          // bit i: matrix i is stored tall
   int final_mode;
@@ -70,13 +75,27 @@ struct WeightTable {       // FINAL_WEIGHTS only
   float scale[kChunk];
 };
 
+// The single kernel argument of each kernel (its tables are read in place
+// from the kernarg segment).
+struct PrepLaunch {
+  PrepArgs a;
+  PrepTable t;
+};
+struct GemmLaunch {
+  GemmArgs a;
+  WeightTable wt;
+};
+
 // Launchers (return hipGetLastError() of the launch).
 hipError_t launch_prep(int grad_bf16, int compute_bf16, int momentum,
                        const PrepArgs& a, const PrepTable& t, int batch,
                        hipStream_t s);
 hipError_t launch_norm(const float* partials, int nblk, float eps, float* inv,
                        int batch, hipStream_t s);
-hipError_t launch_gemm(int compute_bf16, int epi, const GemmArgs& a,
+// Square GEMM tile edge (128 or 256) used for a compute precision, given
+// the caller's preference (0 = default).
+int gemm_tile(int compute_bf16, int tile_pref);
+hipError_t launch_gemm(int compute_bf16, int epi, int tile, const GemmArgs& a,
                        const WeightTable& t, int batch, hipStream_t s);
 
 }  // namespace muon

@@ -18,6 +18,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cstdlib>
+#include <utility>
+
 #include "muon_kernels.h"
 
 namespace muon {
@@ -27,6 +30,13 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Kernel arguments are read in place from the kernarg segment: indexing a
+// per-matrix table with the matrix index must not copy the table to scratch.
+template <typename Arg>
+__device__ __forceinline__ const __attribute__((address_space(4))) Arg& kernarg() {
+  return *(const __attribute__((address_space(4))) Arg*)__builtin_amdgcn_kernarg_segment_ptr();
+}
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16_t x) { return static_cast<float>(x); }
@@ -40,12 +50,25 @@ __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
   return static_cast<bf16_t>(x);  // v_cvt_pk_bf16_f32: round to nearest even
 }
 
+// Compile-time loop: f(std::integral_constant<int, 0>) ... f(<N-1>), so that
+// register arrays are never indexed at run time (which would put them in
+// scratch memory).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // ---------------------------------------------------------------- prep
 // One 64x64 tile of the oriented, padded M x N space per block.  Reads the
 // original matrix coalesced along its rows, writes the copy that shares the
 // original layout directly and the transposed copy through an LDS tile.
 template <typename GT, typename CT, bool MOM>
-__global__ __launch_bounds__(256) void prep_kernel(PrepArgs a, PrepTable t) {
+__global__ __launch_bounds__(256) void prep_kernel(PrepLaunch launch) {
+  const PrepArgs& a = launch.a;
   __shared__ float tile[kPrepTile][kPrepTile + 1];
   __shared__ float red[4];
   const int tid = threadIdx.x;
@@ -61,8 +84,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a, PrepTable t) {
   const GT* g;
   float* buf = nullptr;
   if constexpr (MOM) {
-    g = static_cast<const GT*>(t.g[mat]);
-    buf = t.buf[mat];
+    g = static_cast<const GT*>(kernarg<PrepLaunch>().t.g[mat]);
+    buf = kernarg<PrepLaunch>().t.buf[mat];
   } else {
     g = static_cast<const GT*>(a.in) + (long long)mat * a.s_in;
   }
@@ -145,6 +168,37 @@ __device__ __forceinline__ void tri_decode(int t, int& ti, int& tj) {
   tj = t - i * (i + 1) / 2;
 }
 
+// Workgroups of a launch are dispatched round-robin over the 8 XCDs
+// (workgroup w runs on XCD w % 8, each XCD with its own L2).  Remap so that
+// every XCD works through one contiguous range of logical tiles: the tiles
+// of one matrix, and neighbouring tiles within it, then share an L2.
+__device__ __forceinline__ int xcd_remap(int w, int total) {
+  const int x = w & 7, k = w >> 3;
+  const int q = total >> 3, r = total & 7;
+  return x * q + (x < r ? x : r) + k;
+}
+
+// Logical tile -> (matrix, tile row, tile column).  Full grids go in groups
+// of `group_m` tile rows, column by column, so that the blocks running
+// together on an XCD share a few row panels and a few column panels.
+__device__ __forceinline__ void decode_tile(const GemmArgs& a, int& mat, int& ti, int& tj) {
+  const int total = a.tiles_per_mat * (int)gridDim.y;
+  const int L = xcd_remap((int)blockIdx.x + (int)blockIdx.y * (int)gridDim.x, total);
+  mat = L / a.tiles_per_mat;
+  const int t = L - mat * a.tiles_per_mat;
+  if (a.tri) {
+    tri_decode(t, ti, tj);
+  } else {
+    const int span = a.group_m * a.tiles_n;
+    const int g = t / span;
+    const int first = g * a.group_m;
+    const int gm = a.tiles_m - first < a.group_m ? a.tiles_m - first : a.group_m;
+    const int idx = t - g * span;
+    ti = first + idx % gm;
+    tj = idx / gm;
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ void mma(f32x16_t& acc, const u32x4_t& fa, const u32x4_t& fb);
 
@@ -164,57 +218,99 @@ __device__ __forceinline__ void mma<float>(f32x16_t& acc, const u32x4_t& fa, con
   for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[e], bv[e], acc, 0, 0, 0);
 }
 
-// 128x128 output tile per block of 4 waves (2x2, 64x64 each, 2x2 MFMA 32x32
-// tiles per wave).  K advances in steps of 128 bytes per row (64 bf16 or 32
-// fp32), staged through two LDS buffers; 16-byte chunks of a row are stored
-// at chunk ^ (row & 7) so that the MFMA operand reads are conflict-free.
-template <typename T, int EPI>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a, WeightTable wt) {
-  constexpr int BM = 128, BN = 128;
+// Block tile BM x BN computed by WGM x WGN waves, each owning a
+// (BM/WGM) x (BN/WGN) sub-tile of 32x32 MFMA tiles.  K advances 128 bytes
+// per row (64 bf16 or 32 fp32) per step through two LDS stages; a row's
+// 16-byte chunks are stored at chunk ^ (row & 7) so that both the stores of
+// the loader and the operand reads of the MFMA lanes are free of bank
+// conflicts.  Operand fragments are double-buffered in registers.
+//
+// Epilogue, one 32-row block of the wave tile at a time: first all of its
+// inputs are loaded (C/X values the epilogue combines with), then values
+// are computed and stored.  The accumulators hold, per lane, 4 consecutive
+// rows i of one column j, so row-major C[i][j] outputs are stored directly
+// (consecutive lanes -> consecutive j).  Transposed outputs (the mirrored
+// triangle of A and B, the next step's X^T) are staged in LDS as [j][i]
+// rows and stored as coalesced 16-byte chunks.
+template <typename T, int EPI, int BM, int BN, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch) {
+  const GemmArgs& a = launch.a;
+  constexpr int NT = 64 * WGM * WGN;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
   constexpr int BK = 8 * EPC;
-  __shared__ u32x4_t lds[2][(BM + BN) * 8];
+  constexpr int RPP = NT / 8;               // rows per loader pass
+  constexpr int PA = BM / RPP, PB = BN / RPP;
+  constexpr int STAGE = (BM + BN) * 8;      // 16-byte chunks per stage
+  constexpr int TLD = BM + 8;               // row stride of the transposed tile
+  constexpr size_t MAIN_BYTES = 2 * (size_t)STAGE * 16;
+  constexpr size_t EPI_BYTES = (size_t)BN * TLD * sizeof(T);
+  constexpr size_t LDS_BYTES = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
+  static_assert(PA * RPP == BM && PB * RPP == BN, "tile rows must split over the loader");
+  static_assert(FM * 32 * WGM == BM && FN * 32 * WGN == BN, "wave tiles must be 32-aligned");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
+  u32x4_t* lds = reinterpret_cast<u32x4_t*>(smem);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int mat = blockIdx.y;
-  int ti, tj;
-  if (a.tri) {
-    tri_decode(blockIdx.x, ti, tj);
-  } else {
-    ti = blockIdx.x / a.tiles_n;
-    tj = blockIdx.x - ti * a.tiles_n;
-  }
-  const T* Pm = static_cast<const T*>(a.P) + (long long)mat * a.sP + (long long)ti * BM * a.ldp;
-  const T* Qm = static_cast<const T*>(a.Q) + (long long)mat * a.sQ + (long long)tj * BN * a.ldq;
+  const int wm = wave / WGN, wn = wave % WGN;
+  int mat, ti, tj;
+  decode_tile(a, mat, ti, tj);
+  const T* __restrict__ Pm =
+      static_cast<const T*>(a.P) + (long long)mat * a.sP + (long long)ti * BM * a.ldp;
+  const T* __restrict__ Qm =
+      static_cast<const T*>(a.Q) + (long long)mat * a.sQ + (long long)tj * BN * a.ldq;
 
   const int lch = tid & 7, lrow = tid >> 3;
-  u32x4_t rp[4], rq[4];
+  u32x4_t rp[PA], rq[PB];
   const int nk = a.K / BK;
-
   auto gload = [&](int kt) {
+    const int kofs = kt * BK + lch * EPC;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      rp[s] = *reinterpret_cast<const u32x4_t*>(Pm + (long long)(lrow + 32 * s) * a.ldp + kt * BK + lch * EPC);
-      rq[s] = *reinterpret_cast<const u32x4_t*>(Qm + (long long)(lrow + 32 * s) * a.ldq + kt * BK + lch * EPC);
-    }
+    for (int s = 0; s < PA; ++s)
+      rp[s] = *reinterpret_cast<const u32x4_t*>(Pm + (long long)(lrow + RPP * s) * a.ldp + kofs);
+#pragma unroll
+    for (int s = 0; s < PB; ++s)
+      rq[s] = *reinterpret_cast<const u32x4_t*>(Qm + (long long)(lrow + RPP * s) * a.ldq + kofs);
   };
   auto lstore = [&](int b) {
+    u32x4_t* L = lds + b * STAGE;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int r = lrow + 32 * s;
-      lds[b][r * 8 + (lch ^ (r & 7))] = rp[s];
-      lds[b][(BM + r) * 8 + (lch ^ (r & 7))] = rq[s];
+    for (int s = 0; s < PA; ++s) {
+      const int r = lrow + RPP * s;
+      L[r * 8 + (lch ^ (r & 7))] = rp[s];
+    }
+#pragma unroll
+    for (int s = 0; s < PB; ++s) {
+      const int r = BM + lrow + RPP * s;
+      L[r * 8 + (lch ^ (r & 7))] = rq[s];
     }
   };
 
-  const int wm = wave >> 1, wn = wave & 1;
-  f32x16_t acc[2][2];
+  f32x16_t acc[FM][FN];
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < FM; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
+    for (int ni = 0; ni < FN; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+
+  const int arow = wm * WTM + (lane & 31), brow = BM + wn * WTN + (lane & 31);
+  const int hsel = lane >> 5;
+  u32x4_t fa[2][FM], fb[2][FN];
+  auto fload = [&](const u32x4_t* L, int kk, int slot) {
+    const int ch = 2 * kk + hsel;
+#pragma unroll
+    for (int mi = 0; mi < FM; ++mi) {
+      const int r = arow + mi * 32;
+      fa[slot][mi] = L[r * 8 + (ch ^ (r & 7))];
+    }
+#pragma unroll
+    for (int ni = 0; ni < FN; ++ni) {
+      const int r = brow + ni * 32;
+      fb[slot][ni] = L[r * 8 + (ch ^ (r & 7))];
+    }
+  };
 
   gload(0);
   lstore(0);
@@ -222,91 +318,157 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a, WeightTable wt) {
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < nk) gload(kt + 1);
+    const u32x4_t* L = lds + cur * STAGE;
+    fload(L, 0, 0);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const int ch = 2 * kk + (lane >> 5);
-      u32x4_t fa[2], fb[2];
+      if (kk < 3) fload(L, kk + 1, (kk + 1) & 1);
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi) {
-        const int r = wm * 64 + mi * 32 + (lane & 31);
-        fa[mi] = lds[cur][r * 8 + (ch ^ (r & 7))];
-      }
+      for (int mi = 0; mi < FM; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni) {
-        const int r = wn * 64 + ni * 32 + (lane & 31);
-        fb[ni] = lds[cur][(BM + r) * 8 + (ch ^ (r & 7))];
-      }
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni) mma<T>(acc[mi][ni], fa[mi], fb[ni]);
+        for (int ni = 0; ni < FN; ++ni) mma<T>(acc[mi][ni], fa[kk & 1][mi], fb[kk & 1][ni]);
     }
     if (kt + 1 < nk) lstore(cur ^ 1);
     __syncthreads();
   }
 
-  // Epilogue.  MFMA 32x32 accumulator layout: lane l, register r holds
-  // row 8*(r/4) + 4*(l/32) + r%4, column l%32 of the 32x32 tile.
-  const int i_base = ti * BM + wm * 64, j_base = tj * BN + wn * 64;
+  // ---- epilogue (LDS is free: the last iteration ended with a barrier)
+  const int i_base = ti * BM + wm * WTM, j_base = tj * BN + wn * WTN;
   float alpha = 1.f, scl = 1.f;
   if (a.inv) {
     const float v = a.inv[mat];
     alpha = v * v;
     scl = v;
   }
-  T* C = static_cast<T*>(a.C) + (long long)mat * a.sC;
-  const T* Ain = static_cast<const T*>(a.Ain) + (long long)mat * a.sAin;
-  float* Xf = a.Xf + (long long)mat * a.sXf;
-  bf16_t* Xb = a.Xb ? static_cast<bf16_t*>(a.Xb) + (long long)mat * a.sXf : nullptr;
-  T* XT = static_cast<T*>(a.XTo) + (long long)mat * a.sXT;
-  const bool mirror = ti != tj;
   const bool tall = (a.tall_mask >> mat) & 1ull;
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = i_base + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int j = j_base + ni * 32 + (lane & 31);
-        float v = acc[mi][ni][r];
-        if constexpr (EPI == EPI_GRAM || EPI == EPI_POLY) {
+  // Transposed output of this block: the mirrored tile (GRAM, POLY off the
+  // diagonal) or the next step's X^T (UPDATE).
+  constexpr bool FINAL = EPI == EPI_FINAL_W || EPI == EPI_FINAL_OUT;
+  bool stage_t = false;
+  if constexpr (EPI == EPI_UPDATE) stage_t = true;
+  if constexpr (EPI == EPI_GRAM || EPI == EPI_POLY) stage_t = ti != tj;
+  T* __restrict__ Ts = reinterpret_cast<T*>(smem);
+  T* __restrict__ C = nullptr;
+  const T* __restrict__ Ain = nullptr;
+  float* __restrict__ Xf = nullptr;
+  bf16_t* __restrict__ Xb = nullptr;
+  float* __restrict__ W = nullptr;
+  float wscale = 0.f;
+  if constexpr (EPI == EPI_UPDATE || FINAL) {
+    Xf = a.Xf + (long long)mat * a.sXf;
+    if (a.Xb) Xb = static_cast<bf16_t*>(a.Xb) + (long long)mat * a.sXf;
+    if constexpr (EPI == EPI_FINAL_W) {
+      W = kernarg<GemmLaunch>().wt.w[mat];
+      wscale = a.neg_lr * kernarg<GemmLaunch>().wt.scale[mat];
+    }
+  } else {
+    C = static_cast<T*>(a.C) + (long long)mat * a.sC;
+    if constexpr (EPI == EPI_POLY) Ain = static_cast<const T*>(a.Ain) + (long long)mat * a.sAin;
+  }
+  const int jl0 = wn * WTN + (lane & 31);
+
+  static_for<FM>([&](auto mi) {
+    const int ib = i_base + mi * 32 + 4 * hsel;  // + 8q + t
+    // phase 1: the inputs of this 32-row block
+    float ein[FN][16];
+    float win[EPI == EPI_FINAL_W ? FN : 1][16];
+    static_for<FN>([&](auto ni) {
+      const int j = j_base + ni * 32 + (lane & 31);
+      static_for<16>([&](auto r) {
+        const int i = ib + 8 * (r / 4) + (r % 4);
+        if constexpr (EPI == EPI_POLY) ein[ni][r] = to_f32(Ain[(long long)i * a.ldc + j]);
+        if constexpr (EPI == EPI_UPDATE || FINAL) ein[ni][r] = Xf[(long long)i * a.ldx + j];
+        if constexpr (EPI == EPI_FINAL_W) {
+          // outside the matrix (zero padding) read element 0 and discard it
+          const bool inb = i < a.m && j < a.n;
+          const long long oo = tall ? (long long)j * a.m + i : (long long)i * a.n + j;
+          win[ni][r] = W[inb ? oo : 0];
+        }
+      });
+    });
+    // phase 2: values, direct stores, transposed staging
+    static_for<FN>([&](auto ni) {
+      const int j = j_base + ni * 32 + (lane & 31);
+      static_for<4>([&](auto q) {
+        float v[4];
+        static_for<4>([&](auto t) {
+          constexpr int r = 4 * q + t;
+          const int i = ib + 8 * q + t;
+          const float accv = acc[mi][ni][r];
           if constexpr (EPI == EPI_GRAM) {
-            v *= alpha;
-          } else {
-            v = a.b * to_f32(Ain[(long long)i * a.ldc + j]) + a.c * v;
-          }
-          const T o = from_f32<T>(v);
-          C[(long long)i * a.ldc + j] = o;
-          if (mirror) C[(long long)j * a.ldc + i] = o;
-        } else {
-          const long long o = (long long)i * a.ldx + j;
-          const float x = scl * (a.a * Xf[o] + v);
-          if (!a.last) {
-            Xf[o] = x;
-            if (Xb) Xb[o] = from_f32<bf16_t>(x);
-            XT[(long long)j * a.ldxt + i] = from_f32<T>(x);
-          } else if (i < a.m && j < a.n) {
-            const long long oo = tall ? (long long)j * a.m + i : (long long)i * a.n + j;
-            if (a.final_mode == FINAL_OUT) {
-              if (a.out_bf16)
+            v[t] = accv * alpha;
+            C[(long long)i * a.ldc + j] = from_f32<T>(v[t]);
+          } else if constexpr (EPI == EPI_POLY) {
+            v[t] = a.b * ein[ni][r] + a.c * accv;
+            C[(long long)i * a.ldc + j] = from_f32<T>(v[t]);
+          } else if constexpr (EPI == EPI_UPDATE) {
+            v[t] = scl * (a.a * ein[ni][r] + accv);
+            const long long o = (long long)i * a.ldx + j;
+            Xf[o] = v[t];
+            if (Xb) Xb[o] = from_f32<bf16_t>(v[t]);
+          } else {  // FINAL_W, FINAL_OUT
+            const float x = scl * (a.a * ein[ni][r] + accv);
+            if (i < a.m && j < a.n) {
+              const long long oo = tall ? (long long)j * a.m + i : (long long)i * a.n + j;
+              if constexpr (EPI == EPI_FINAL_W) {
+                W[oo] = fmaf(wscale, x, win[ni][r]);
+              } else if (a.out_bf16) {
                 static_cast<bf16_t*>(a.out)[(long long)mat * a.s_out + oo] = from_f32<bf16_t>(x);
-              else
+              } else {
                 static_cast<float*>(a.out)[(long long)mat * a.s_out + oo] = x;
-            } else if (a.final_mode == FINAL_WEIGHTS) {
-              float* W = wt.w[mat];
-              W[oo] = fmaf(a.neg_lr * wt.scale[mat], x, W[oo]);
+              }
+            }
+          }
+        });
+        if constexpr (!FINAL) {
+          if (stage_t) {
+            const int il = wm * WTM + mi * 32 + 8 * q + 4 * hsel, jl = jl0 + ni * 32;
+            if constexpr (sizeof(T) == 2) {
+              uint2 pk;
+              pk.x = (unsigned)__builtin_bit_cast(unsigned short, from_f32<T>(v[0])) |
+                     ((unsigned)__builtin_bit_cast(unsigned short, from_f32<T>(v[1])) << 16);
+              pk.y = (unsigned)__builtin_bit_cast(unsigned short, from_f32<T>(v[2])) |
+                     ((unsigned)__builtin_bit_cast(unsigned short, from_f32<T>(v[3])) << 16);
+              *reinterpret_cast<uint2*>(Ts + jl * TLD + il) = pk;
+            } else {
+              f32x4_t f;
+              f[0] = v[0]; f[1] = v[1]; f[2] = v[2]; f[3] = v[3];
+              *reinterpret_cast<f32x4_t*>(Ts + jl * TLD + il) = f;
             }
           }
         }
+      });
+    });
+  });
+  if constexpr (!FINAL) {
+    if (stage_t) {
+      __syncthreads();
+      T* __restrict__ dst;
+      int ld;
+      if constexpr (EPI == EPI_UPDATE) {
+        dst = static_cast<T*>(a.XTo) + (long long)mat * a.sXT;
+        ld = a.ldxt;
+      } else {
+        dst = C;
+        ld = a.ldc;
       }
+      constexpr int CPR = BM / EPC;  // 16-byte chunks per transposed row
+#pragma unroll 4
+      for (int c = tid; c < BN * CPR; c += NT) {
+        const int jl = c / CPR, il = (c % CPR) * EPC;
+        *reinterpret_cast<u32x4_t*>(dst + (long long)(tj * BN + jl) * ld + ti * BM + il) =
+            *reinterpret_cast<const u32x4_t*>(Ts + jl * TLD + il);
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------- launchers
 hipError_t launch_prep(int grad_bf16, int compute_bf16, int momentum, const PrepArgs& a,
                        const PrepTable& t, int batch, hipStream_t s) {
   const dim3 grid(a.nblk, batch), block(256);
-#define MUON_PREP(GT, CT, MOM) hipLaunchKernelGGL((prep_kernel<GT, CT, MOM>), grid, block, 0, s, a, t)
+  const PrepLaunch launch{a, t};
+#define MUON_PREP(GT, CT, MOM) hipLaunchKernelGGL((prep_kernel<GT, CT, MOM>), grid, block, 0, s, launch)
   if (grad_bf16) {
     if (compute_bf16) {
       if (momentum) MUON_PREP(bf16_t, bf16_t, true); else MUON_PREP(bf16_t, bf16_t, false);
@@ -330,21 +492,64 @@ hipError_t launch_norm(const float* partials, int nblk, float eps, float* inv, i
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(int compute_bf16, int epi, const GemmArgs& a, const WeightTable& t,
-                       int batch, hipStream_t s) {
-  const int tiles = a.tri ? a.tiles_m * (a.tiles_m + 1) / 2 : a.tiles_m * a.tiles_n;
-  const dim3 grid(tiles, batch), block(256);
-#define MUON_GEMM(T, E) hipLaunchKernelGGL((gemm_kernel<T, E>), grid, block, 0, s, a, t)
-  if (compute_bf16) {
-    if (epi == EPI_GRAM) MUON_GEMM(bf16_t, EPI_GRAM);
-    else if (epi == EPI_POLY) MUON_GEMM(bf16_t, EPI_POLY);
-    else MUON_GEMM(bf16_t, EPI_UPDATE);
-  } else {
-    if (epi == EPI_GRAM) MUON_GEMM(float, EPI_GRAM);
-    else if (epi == EPI_POLY) MUON_GEMM(float, EPI_POLY);
-    else MUON_GEMM(float, EPI_UPDATE);
+int gemm_tile(int compute_bf16, int tile_pref) {
+  if (!compute_bf16) return 128;
+  return tile_pref == 128 ? 128 : 256;
+}
+
+// bf16 block shapes: 0 = 256x256 by 4 waves (128x128 each), 1 = 256x256 by
+// 8 waves (2x4, 128x64 each), 2 = 256x256 by 8 waves (4x2, 64x128 each);
+// 128x128 tiles always use 4 waves (64x64 each).
+static int wave_cfg() {
+  static const int v = [] {
+    const char* e = std::getenv("MUON_WAVE_CFG");
+    return e ? std::atoi(e) : 1;
+  }();
+  return v;
+}
+
+template <typename T, int E>
+static void launch_gemm_t(int tile, const GemmArgs& a, const WeightTable& t, dim3 grid,
+                          hipStream_t s) {
+  const GemmLaunch launch{a, t};
+  if constexpr (sizeof(T) == 2) {
+    if (tile == 256) {
+      switch (wave_cfg()) {
+        case 0:
+          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 2>), grid, dim3(256), 0, s, launch);
+          return;
+        case 2:
+          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 4, 2>), grid, dim3(512), 0, s, launch);
+          return;
+        default:
+          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4>), grid, dim3(512), 0, s, launch);
+          return;
+      }
+    }
   }
-#undef MUON_GEMM
+  hipLaunchKernelGGL((gemm_kernel<T, E, 128, 128, 2, 2>), grid, dim3(256), 0, s, launch);
+}
+
+hipError_t launch_gemm(int compute_bf16, int epi, int tile, const GemmArgs& a_in,
+                       const WeightTable& t, int batch, hipStream_t s) {
+  GemmArgs a = a_in;
+  a.tiles_per_mat = a.tri ? a.tiles_m * (a.tiles_m + 1) / 2 : a.tiles_m * a.tiles_n;
+  // grid.y = matrices, grid.x = tiles; the kernel linearises and remaps both
+  const dim3 grid(a.tiles_per_mat, batch);
+  if (compute_bf16) {
+    if (epi == EPI_GRAM) launch_gemm_t<bf16_t, EPI_GRAM>(tile, a, t, grid, s);
+    else if (epi == EPI_POLY) launch_gemm_t<bf16_t, EPI_POLY>(tile, a, t, grid, s);
+    else if (epi == EPI_UPDATE) launch_gemm_t<bf16_t, EPI_UPDATE>(tile, a, t, grid, s);
+    else if (epi == EPI_FINAL_W) launch_gemm_t<bf16_t, EPI_FINAL_W>(tile, a, t, grid, s);
+    else launch_gemm_t<bf16_t, EPI_FINAL_OUT>(tile, a, t, grid, s);
+  } else {
+    // fp32 path: 128 x 128 tiles (the transposed epilogue tile fits in LDS)
+    if (epi == EPI_GRAM) launch_gemm_t<float, EPI_GRAM>(128, a, t, grid, s);
+    else if (epi == EPI_POLY) launch_gemm_t<float, EPI_POLY>(128, a, t, grid, s);
+    else if (epi == EPI_UPDATE) launch_gemm_t<float, EPI_UPDATE>(128, a, t, grid, s);
+    else if (epi == EPI_FINAL_W) launch_gemm_t<float, EPI_FINAL_W>(128, a, t, grid, s);
+    else launch_gemm_t<float, EPI_FINAL_OUT>(128, a, t, grid, s);
+  }
   return hipGetLastError();
 }
 
