@@ -199,6 +199,18 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& a, int& mat, int& ti
   }
 }
 
+// LDS slot of 16-byte chunk `c` of tile row `r`, rows of CPR chunks.  The
+// LDS has 64 four-byte banks (256 bytes) and serves 16 lanes of a 16-byte
+// access per cycle; 256 / (16 CPR) rows share one bank line, so the chunk
+// order is permuted by the index of the row's bank line: 16 consecutive rows
+// at one chunk then hit 16 distinct bank groups (MFMA operand reads), and the
+// CPR lanes writing one row stay distinct (loader stores).
+template <int CPR>
+__device__ __forceinline__ int swz(int c, int r) {
+  constexpr int RPL = 16 / CPR;  // rows per 256-byte bank line
+  return c ^ ((r / RPL) % CPR);
+}
+
 template <typename T>
 __device__ __forceinline__ void mma(f32x16_t& acc, const u32x4_t& fa, const u32x4_t& fb);
 
@@ -221,9 +233,8 @@ __device__ __forceinline__ void mma<float>(f32x16_t& acc, const u32x4_t& fa, con
 // Block tile BM x BN computed by WGM x WGN waves, each owning a
 // (BM/WGM) x (BN/WGN) sub-tile of 32x32 MFMA tiles.  K advances 128 bytes
 // per row (64 bf16 or 32 fp32) per step through two LDS stages; a row's
-// 16-byte chunks are stored at chunk ^ (row & 7) so that both the stores of
-// the loader and the operand reads of the MFMA lanes are free of bank
-// conflicts.  Operand fragments are double-buffered in registers.
+// 16-byte chunks are permuted (swz) so that both the stores of the loader
+// and the operand reads of the MFMA lanes are free of bank conflicts.  Operand fragments are double-buffered in registers.
 //
 // Epilogue, one 32-row block of the wave tile at a time: first all of its
 // inputs are loaded (C/X values the epilogue combines with), then values
@@ -232,23 +243,65 @@ __device__ __forceinline__ void mma<float>(f32x16_t& acc, const u32x4_t& fa, con
 // (consecutive lanes -> consecutive j).  Transposed outputs (the mirrored
 // triangle of A and B, the next step's X^T) are staged in LDS as [j][i]
 // rows and stored as coalesced 16-byte chunks.
-template <typename T, int EPI, int BM, int BN, int WGM, int WGN>
+// Wait until at most N vector-memory operations of this wave are in flight
+// (other counters untouched): s_waitcnt with vmcnt = N, expcnt = 7,
+// lgkmcnt = 15.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the kernel stub
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+#endif
+}
+
+// Workgroup barrier for the direct-to-LDS pipeline, without memory fences:
+// a fence would wait for every outstanding load, including the loads of
+// later k-tiles that must stay in flight.  It is sufficient here because
+// (1) each wave waits (vmcnt) for its own loads of the k-tile about to be
+// read before arriving, and LDS has no cache, so the data is in place for
+// every wave once all have arrived; (2) a wave's LDS reads of the stage that
+// is reloaded next have returned before its MFMAs consumed them.  The
+// "memory" clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier_no_fence() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_barrier" ::: "memory");
+#endif
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l writes
+// lds_wave_base + 16 l (lds_wave_base must be the same for the whole wave).
+__device__ __forceinline__ void load_lds16(const void* src, void* lds_wave_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, lds_wave_base, 16, 0, 0);
+#endif
+}
+
+// Main loop variants (template parameter S):
+//  S == 0  operands go global -> registers -> LDS, two LDS stages, the next
+//          k-tile's loads in flight while the current one is multiplied;
+//  S >= 2  operands go global -> LDS directly (global_load_lds_dwordx4:
+//          lane l of a wave writes 16 bytes at the wave's LDS address + 16 l),
+//          S LDS stages, loads issued S - 1 k-tiles ahead.
+// RB is the bytes of one operand row per k-tile (64 or 128).
+template <typename T, int EPI, int BM, int BN, int WGM, int WGN, int S, int RB, bool SCHED = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch) {
   const GemmArgs& a = launch.a;
-  constexpr int NT = 64 * WGM * WGN;
+  constexpr int NT = 64 * WGM * WGN, NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
-  constexpr int BK = 8 * EPC;
-  constexpr int RPP = NT / 8;               // rows per loader pass
-  constexpr int PA = BM / RPP, PB = BN / RPP;
-  constexpr int STAGE = (BM + BN) * 8;      // 16-byte chunks per stage
+  constexpr int CPR = RB / 16;              // chunks per operand row and k-tile
+  constexpr int BK = CPR * EPC;             // k per k-tile
+  constexpr int KK = CPR / 2;               // MFMA k-substeps per k-tile
+  constexpr int ROWS = BM + BN;             // P rows, then Q rows
+  constexpr int STAGE = ROWS * CPR;         // 16-byte chunks per stage
+  constexpr int NSTAGE = S == 0 ? 2 : S;
   constexpr int TLD = BM + 8;               // row stride of the transposed tile
-  constexpr size_t MAIN_BYTES = 2 * (size_t)STAGE * 16;
+  constexpr size_t MAIN_BYTES = (size_t)NSTAGE * STAGE * 16;
   constexpr size_t EPI_BYTES = (size_t)BN * TLD * sizeof(T);
   constexpr size_t LDS_BYTES = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
-  static_assert(PA * RPP == BM && PB * RPP == BN, "tile rows must split over the loader");
   static_assert(FM * 32 * WGM == BM && FN * 32 * WGN == BN, "wave tiles must be 32-aligned");
+  static_assert(S == 0 ? RB == 128 : S >= 2, "register path uses 128-byte rows");
   __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
   u32x4_t* lds = reinterpret_cast<u32x4_t*>(smem);
 
@@ -260,32 +313,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
       static_cast<const T*>(a.P) + (long long)mat * a.sP + (long long)ti * BM * a.ldp;
   const T* __restrict__ Qm =
       static_cast<const T*>(a.Q) + (long long)mat * a.sQ + (long long)tj * BN * a.ldq;
-
-  const int lch = tid & 7, lrow = tid >> 3;
-  u32x4_t rp[PA], rq[PB];
   const int nk = a.K / BK;
-  auto gload = [&](int kt) {
-    const int kofs = kt * BK + lch * EPC;
-#pragma unroll
-    for (int s = 0; s < PA; ++s)
-      rp[s] = *reinterpret_cast<const u32x4_t*>(Pm + (long long)(lrow + RPP * s) * a.ldp + kofs);
-#pragma unroll
-    for (int s = 0; s < PB; ++s)
-      rq[s] = *reinterpret_cast<const u32x4_t*>(Qm + (long long)(lrow + RPP * s) * a.ldq + kofs);
-  };
-  auto lstore = [&](int b) {
-    u32x4_t* L = lds + b * STAGE;
-#pragma unroll
-    for (int s = 0; s < PA; ++s) {
-      const int r = lrow + RPP * s;
-      L[r * 8 + (lch ^ (r & 7))] = rp[s];
-    }
-#pragma unroll
-    for (int s = 0; s < PB; ++s) {
-      const int r = BM + lrow + RPP * s;
-      L[r * 8 + (lch ^ (r & 7))] = rq[s];
-    }
-  };
 
   f32x16_t acc[FM][FN];
 #pragma unroll
@@ -303,32 +331,124 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
 #pragma unroll
     for (int mi = 0; mi < FM; ++mi) {
       const int r = arow + mi * 32;
-      fa[slot][mi] = L[r * 8 + (ch ^ (r & 7))];
+      fa[slot][mi] = L[r * CPR + swz<CPR>(ch, r)];
     }
 #pragma unroll
     for (int ni = 0; ni < FN; ++ni) {
       const int r = brow + ni * 32;
-      fb[slot][ni] = L[r * 8 + (ch ^ (r & 7))];
+      fb[slot][ni] = L[r * CPR + swz<CPR>(ch, r)];
     }
   };
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const u32x4_t* L = lds + cur * STAGE;
+  auto compute = [&](const u32x4_t* L) {
     fload(L, 0, 0);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      if (kk < 3) fload(L, kk + 1, (kk + 1) & 1);
+    for (int kk = 0; kk < KK; ++kk) {
+      if (kk + 1 < KK) fload(L, kk + 1, (kk + 1) & 1);
 #pragma unroll
       for (int mi = 0; mi < FM; ++mi)
 #pragma unroll
         for (int ni = 0; ni < FN; ++ni) mma<T>(acc[mi][ni], fa[kk & 1][mi], fb[kk & 1][ni]);
     }
-    if (kt + 1 < nk) lstore(cur ^ 1);
+    if constexpr (S >= 2 && SCHED) {
+      // Pinned order: the first substep's reads, then each later substep's
+      // reads one after each MFMA of the substep before it.
+      __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
+#pragma unroll
+      for (int kk = 0; kk + 1 < KK; ++kk) {
+#pragma unroll
+        for (int x = 0; x < FM + FN; ++x) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
+    }
+  };
+
+  if constexpr (S == 0) {
+    constexpr int RPP = NT / 8;  // rows per loader pass
+    constexpr int PA = BM / RPP, PB = BN / RPP;
+    static_assert(PA * RPP == BM && PB * RPP == BN, "tile rows must split over the loader");
+    const int lch = tid & 7, lrow = tid >> 3;
+    u32x4_t rp[PA], rq[PB];
+    auto gload = [&](int kt) {
+      const int kofs = kt * BK + lch * EPC;
+#pragma unroll
+      for (int s = 0; s < PA; ++s)
+        rp[s] = *reinterpret_cast<const u32x4_t*>(Pm + (long long)(lrow + RPP * s) * a.ldp + kofs);
+#pragma unroll
+      for (int s = 0; s < PB; ++s)
+        rq[s] = *reinterpret_cast<const u32x4_t*>(Qm + (long long)(lrow + RPP * s) * a.ldq + kofs);
+    };
+    auto lstore = [&](int b) {
+      u32x4_t* L = lds + b * STAGE;
+#pragma unroll
+      for (int s = 0; s < PA; ++s) {
+        const int r = lrow + RPP * s;
+        L[r * 8 + swz<8>(lch, r)] = rp[s];
+      }
+#pragma unroll
+      for (int s = 0; s < PB; ++s) {
+        const int r = BM + lrow + RPP * s;
+        L[r * 8 + swz<8>(lch, r)] = rq[s];
+      }
+    };
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      if (kt + 1 < nk) gload(kt + 1);
+      compute(lds + cur * STAGE);
+      if (kt + 1 < nk) lstore(cur ^ 1);
+      __syncthreads();
+    }
+  } else {
+    // Direct-to-LDS loads.  One instruction moves 64 x 16 bytes = RPI rows;
+    // each wave owns DPW of them per stage.  Lane l fills LDS slot l % CPR of
+    // row l / CPR, so it fetches the global chunk that the swizzle puts there.
+    constexpr int RPI = 1024 / RB;
+    constexpr int DPW = ROWS / RPI / NW;
+    static_assert(DPW * RPI * NW == ROWS, "stage rows must split over the waves");
+    static_assert(DPW * (S - 2) < 64, "vmcnt range");
+    const T* src[DPW];
+#pragma unroll
+    for (int d = 0; d < DPW; ++d) {
+      const int r = (wave * DPW + d) * RPI + lane / CPR;
+      const int c = swz<CPR>(lane % CPR, r);
+      src[d] = r < BM ? Pm + (long long)r * a.ldp + c * EPC
+                      : Qm + (long long)(r - BM) * a.ldq + c * EPC;
+    }
+    auto issue = [&](int kt, int stage) {
+#pragma unroll
+      for (int d = 0; d < DPW; ++d)
+        load_lds16(src[d] + (long long)kt * BK,
+                   smem + (size_t)stage * STAGE * 16 + (size_t)(wave * DPW + d) * 1024);
+    };
+#pragma unroll
+    for (int t = 0; t < S - 1; ++t)
+      if (t < nk) issue(t, t);
+    for (int kt0 = 0; kt0 < nk; kt0 += S) {
+      static_for<S>([&](auto st) {
+        const int kt = kt0 + st;
+        if (kt < nk) {
+          // this wave's loads of k-tile kt have landed once at most
+          // min(S - 2, k-tiles issued after it) load groups are in flight
+          const int later = nk - 1 - kt;
+          if (later >= S - 2) {
+            wait_vmcnt<DPW * (S - 2)>();
+          } else {
+            static_for<S - 2>([&](auto q) {
+              if (later == q) wait_vmcnt<DPW * q>();
+            });
+          }
+          barrier_no_fence();  // every wave's loads of kt are in LDS; stage kt-1 is free
+          if (kt + S - 1 < nk) issue(kt + S - 1, (st + S - 1) % S);
+          compute(lds + st * STAGE);
+        }
+      });
+    }
     __syncthreads();
   }
 
@@ -497,13 +617,17 @@ int gemm_tile(int compute_bf16, int tile_pref) {
   return tile_pref == 128 ? 128 : 256;
 }
 
-// bf16 block shapes: 0 = 256x256 by 4 waves (128x128 each), 1 = 256x256 by
-// 8 waves (2x4, 128x64 each), 2 = 256x256 by 8 waves (4x2, 64x128 each);
-// 128x128 tiles always use 4 waves (64x64 each).
+// bf16 256x256 tiles on 8 waves (2x4, 128x64 each).  Main loop, chosen by
+// MUON_WAVE_CFG (a tuning knob; default 4):
+//   0  register-staged loads, 128-byte rows, two LDS stages
+//   1  direct-to-LDS loads, 64-byte rows, 3 stages
+//   3  as 1 with the MFMA / LDS-read order pinned
+//   4  direct-to-LDS loads, 128-byte rows, 2 stages, order pinned
+// 128x128 tiles use 4 waves (64x64 each) and register-staged loads.
 static int wave_cfg() {
   static const int v = [] {
     const char* e = std::getenv("MUON_WAVE_CFG");
-    return e ? std::atoi(e) : 1;
+    return e ? std::atoi(e) : 4;
   }();
   return v;
 }
@@ -516,18 +640,25 @@ static void launch_gemm_t(int tile, const GemmArgs& a, const WeightTable& t, dim
     if (tile == 256) {
       switch (wave_cfg()) {
         case 0:
-          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 2>), grid, dim3(256), 0, s, launch);
+          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 0, 128>), grid, dim3(512), 0, s,
+                             launch);
           return;
-        case 2:
-          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 4, 2>), grid, dim3(512), 0, s, launch);
+        case 1:
+          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 3, 64>), grid, dim3(512), 0, s,
+                             launch);
+          return;
+        case 3:
+          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 3, 64, true>), grid, dim3(512), 0,
+                             s, launch);
           return;
         default:
-          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4>), grid, dim3(512), 0, s, launch);
+          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 2, 128, true>), grid, dim3(512), 0,
+                             s, launch);
           return;
       }
     }
   }
-  hipLaunchKernelGGL((gemm_kernel<T, E, 128, 128, 2, 2>), grid, dim3(256), 0, s, launch);
+  hipLaunchKernelGGL((gemm_kernel<T, E, 128, 128, 2, 2, 0, 128>), grid, dim3(256), 0, s, launch);
 }
 
 hipError_t launch_gemm(int compute_bf16, int epi, int tile, const GemmArgs& a_in,
