@@ -31,8 +31,13 @@ def parse():
     p.add_argument("--workload", default="gpt_3.8b_28layers")
     p.add_argument("--compute", default="bf16", choices=["bf16", "fp32"])
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-budget", type=float, default=30.0,
-                   help="seconds of oracle work at most for the CPU baseline")
+    p.add_argument("--cpu-sample-seconds", type=float, default=12.0,
+                   help="seconds of oracle work for the CPU baseline sample")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="also run one plain 1 GiB device copy (traffic counter calibration)")
+    p.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of a "
+                        "'--steps 1 --warmup 0 --calibrate-copy' run into profiles/traffic.json")
     return p.parse_args()
 
 
@@ -56,29 +61,92 @@ def kernel_summary(records, steps):
     return out
 
 
+KERNEL_SRC = os.path.join(ROOT, "muon_newton_schulz_step_amd", "csrc", "muon_kernels.hip")
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+COPY_BYTES = 1 << 30
+
+
+def kernel_source_digest():
+    import hashlib
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+
+
 def traffic_from_profiles(kernel_key):
-    """HBM bytes per launch of the dominant kernel from a committed rocprofv3
-    PMC summary, if one exists for the current kernel source."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
+    """HBM bytes per launch of a kernel from the committed counter summary,
+    or None if there is none for the current kernel source."""
+    if not os.path.exists(TRAFFIC_JSON):
         return None
     try:
-        import hashlib
-        with open(path) as f:
+        with open(TRAFFIC_JSON) as f:
             data = json.load(f)
-        src = os.path.join(ROOT, "muon_newton_schulz_step_amd", "csrc", "muon_kernels.hip")
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-        if data.get("kernel_source_sha256") != digest:
+        if data.get("kernel_source_sha256") != kernel_source_digest():
             return None
-        return data.get("kernels", {}).get(kernel_key)
+        k = data["kernels"].get(kernel_key)
+        return None if k is None else k["traffic_bytes"]
     except Exception:
         return None
 
 
-def cpu_baseline(w, budget_s):
-    """fp64 oracle on a bounded sample: one matrix of every oriented group,
-    extrapolated by the group counts to the full step."""
-    import numpy as np
+def launch_sequence(w):
+    """(kind, m, n) of every library launch of one step, in launch order."""
+    seq = []
+    for (m, n), cnt in w.oriented_groups().items():
+        for _ in range(0, cnt, 64):
+            seq += [("prep", m, n), ("norm", m, n)]
+            for k in range(w.n_steps):
+                seq += [("gram", m, n), ("poly", m, n),
+                        ("update" if k < w.n_steps - 1 else "final", m, n)]
+    return seq
+
+
+def write_traffic(fetch_csv, write_csv, w):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of one profiled step,
+    scaled by what the same counters read for a plain copy kernel of
+    COPY_BYTES read + COPY_BYTES written (an elementwise multiply by 1)."""
+    import csv
+
+    def per_dispatch(path, counter):
+        rows = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            did = int(r["Dispatch_Id"])
+            rows.setdefault(did, [r["Kernel_Name"], 0.0])
+            rows[did][1] += float(r["Counter_Value"])
+        return [rows[k] for k in sorted(rows)]
+
+    out = {"kernel_source_sha256": kernel_source_digest(), "copy_bytes": COPY_BYTES,
+           "workload": w.name, "kernels": {}}
+    seq = launch_sequence(w)
+    for path, counter, field in ((fetch_csv, "FETCH_SIZE", "fetch"),
+                                 (write_csv, "WRITE_SIZE", "write")):
+        rows = per_dispatch(path, counter)
+        first = next(i for i, (name, _) in enumerate(rows) if "muon" in name)
+        copy_kib = rows[first - 1][1]  # the calibration copy runs right before the step
+        scale = COPY_BYTES / (copy_kib * 1024.0)
+        out[field + "_scale"] = scale
+        muon = [v for name, v in rows if "muon" in name]
+        if len(muon) != len(seq):
+            raise SystemExit(f"{len(muon)} library dispatches in {path}, expected {len(seq)}")
+        acc = {}
+        for (kind, m, n), v in zip(seq, muon):
+            a = acc.setdefault(f"{kind}_{m}x{n}", [0, 0.0])
+            a[0] += 1
+            a[1] += v * 1024.0 * scale
+        for key, (cnt, tot) in acc.items():
+            out["kernels"].setdefault(key, {})[field + "_bytes"] = tot / cnt
+    for k in out["kernels"].values():
+        k["traffic_bytes"] = k["fetch_bytes"] + k["write_bytes"]
+    os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+    print(f"wrote {TRAFFIC_JSON}")
+
+
+def cpu_baseline(w, seconds):
+    """The fp64 oracle on a bounded sample of the workload: matrices taken
+    round-robin over the oriented groups until about `seconds` of CPU work,
+    per-group mean times extrapolated by the group counts."""
     import oracle
     import workloads as wl
     try:
@@ -88,33 +156,37 @@ def cpu_baseline(w, budget_s):
     except Exception:
         threads = os.cpu_count()
     groups = w.oriented_groups()
-    first = {}
+    members = {}
     for i, (r, c) in enumerate(w.shapes):
-        first.setdefault((min(r, c), max(r, c)), i)
-    order = sorted(groups, key=lambda k: k[0] * k[0] * k[1])
-    total_ms, done, spent = 0.0, [], 0.0
-    for key in order:
-        idx = first[key]
-        x = wl.make_inputs(w, device="cpu", indices=[idx])
-        g = x["grads"][0].double().numpy()
-        b = x["bufs"][0].double().numpy()
-        p = x["params"][0].double().numpy()
-        t0 = time.perf_counter()
-        oracle.muon_step(p, g, b, w.mu, w.lr, x["scales"][0], w.coeff_table)
-        dt = time.perf_counter() - t0
-        spent += dt
-        total_ms += dt * 1e3 * groups[key]
-        done.append(f"{key[0]}x{key[1]}")
-        if spent > budget_s:
+        members.setdefault((min(r, c), max(r, c)), []).append(i)
+    times = {k: [] for k in groups}
+    spent, rnd = 0.0, 0
+    while True:
+        for key in groups:
+            if rnd >= len(members[key]):
+                continue
+            idx = members[key][rnd]
+            x = wl.make_inputs(w, device="cpu", indices=[idx])
+            g = x["grads"][0].double().numpy()
+            b = x["bufs"][0].double().numpy()
+            p = x["params"][0].double().numpy()
+            t0 = time.perf_counter()
+            oracle.muon_step(p, g, b, w.mu, w.lr, x["scales"][0], w.coeff_table)
+            dt = time.perf_counter() - t0
+            times[key].append(dt)
+            spent += dt
+        rnd += 1
+        if spent >= seconds or rnd >= max(len(v) for v in members.values()):
             break
-    complete = len(done) == len(order)
+    total_ms = sum(1e3 * sum(t) / len(t) * groups[k] for k, t in times.items())
+    sample = ", ".join(f"{len(times[k])} x {k[0]}x{k[1]}" for k in groups)
     return {
-        "value": total_ms if complete else None,
-        "unit": "ms per step (extrapolated)",
+        "value": round(total_ms, 1),
+        "unit": "ms per step (extrapolated from the sample)",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"one matrix per oriented group ({', '.join(done)}), fp64 numpy, "
-                   f"x group counts {[groups[k] for k in order]}; {spent:.1f} s of CPU work"),
+        "sample": (f"fp64 numpy Muon step on {sample} matrices (of {len(w.shapes)}), "
+                   f"{spent:.1f} s of CPU work; per-group mean x group count"),
     }
 
 
@@ -130,6 +202,9 @@ def main():
     import workloads as wl
 
     w = wl.WORKLOADS[args.workload]
+    if args.write_traffic:
+        write_traffic(args.write_traffic[0], args.write_traffic[1], w)
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     inputs = wl.make_inputs(w, device=dev)
@@ -141,6 +216,12 @@ def main():
                 scales=inputs["scales"], coeffs=w.coeff_table, compute=args.compute,
                 workspace=ws)
 
+    if args.calibrate_copy:
+        src = torch.ones(COPY_BYTES // 4, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)  # one elementwise kernel: reads and writes COPY_BYTES
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
@@ -161,14 +242,14 @@ def main():
     ms_per_step = e0.elapsed_time(e1) / args.steps
     records = mn.timing_read()
     kernels = kernel_summary(records, args.steps)
-    ns = [k for k in kernels if k["kind"] in ("gram", "poly", "update")]
+    ns = [k for k in kernels if k["kind"] in ("gram", "poly", "update", "final")]
     ns_ms = sum(k["ms"] for k in ns) / args.steps
     flops = w.ns_flops_counted()
     ns_tflops = flops / (ns_ms * 1e-3) / 1e12
     step_tflops = flops / (ms_per_step * 1e-3) / 1e12
     dom = kernels[0]
     dom_key = f"{dom['kind']}_{dom['m']}x{dom['n']}"
-    bound = "mfma" if dom["kind"] in ("gram", "poly", "update") else "hbm"
+    bound = "mfma" if dom["kind"] in ("gram", "poly", "update", "final") else "hbm"
     if bound == "mfma":
         achieved = dom["flops"] / dom["launches"] / (dom["avg_launch_ms"] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK[args.compute],
@@ -183,7 +264,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, args.cpu_sample_budget)
+        cpu = cpu_baseline(w, args.cpu_sample_seconds)
 
     groups = w.oriented_groups()
     out = {

@@ -138,7 +138,8 @@ typedef enum {
   MUON_K_NORM = 1,   /* per-matrix 1 / (||u||_F + eps) */
   MUON_K_GRAM = 2,   /* A = X X^T, one triangle, mirrored */
   MUON_K_POLY = 3,   /* B = b A + c A^2 */
-  MUON_K_UPDATE = 4  /* X <- a X + B X (last step: weight update or output) */
+  MUON_K_UPDATE = 4, /* X <- a X + B X, steps before the last */
+  MUON_K_FINAL = 5   /* last step's a X + B X, written to the weights or output */
 } muon_kernel_kind;
 
 typedef struct {
@@ -147,7 +148,7 @@ typedef struct {
   int batch;       /* matrices in the launch */
   int step;        /* Newton-Schulz step, -1 for PREP and NORM */
   float ms;        /* elapsed time between HIP events around the launch */
-  double flops;    /* counted flops: GRAM 2m^2n, POLY 2m^3, UPDATE 2m^2n per matrix */
+  double flops;    /* counted flops: GRAM 2m^2n, POLY 2m^3, UPDATE/FINAL 2m^2n per matrix */
   double bytes;    /* algorithmic HBM bytes of the launch (see the design notes) */
 } muon_timing_record;
 

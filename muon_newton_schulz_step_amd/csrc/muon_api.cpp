@@ -236,7 +236,8 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
         cnt * ((double)MM * es + (double)MN * es + (double)MN * 4.0) +
         (last ? (c.final_mode == FINAL_WEIGHTS ? elems * 8.0 : elems * (c.out_bf16 ? 2.0 : 4.0))
               : cnt * (double)MN * (4.0 + es + (cbf16 ? 2.0 : 0.0)));
-    err = timed(MUON_K_UPDATE, L.m, L.n, c.cnt, k, cnt * 2.0 * m * m * n, upd_bytes, s,
+    err = timed(last ? MUON_K_FINAL : MUON_K_UPDATE, L.m, L.n, c.cnt, k, cnt * 2.0 * m * m * n,
+                upd_bytes, s,
                 [&] { return launch_gemm(cbf16, !last ? EPI_UPDATE
                                              : c.final_mode == FINAL_WEIGHTS ? EPI_FINAL_W
                                                                              : EPI_FINAL_OUT,
