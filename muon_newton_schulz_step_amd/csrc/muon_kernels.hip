@@ -283,7 +283,8 @@ __device__ __forceinline__ void load_lds16(const void* src, void* lds_wave_base)
 //          lane l of a wave writes 16 bytes at the wave's LDS address + 16 l),
 //          S LDS stages, loads issued S - 1 k-tiles ahead.
 // RB is the bytes of one operand row per k-tile (64 or 128).
-template <typename T, int EPI, int BM, int BN, int WGM, int WGN, int S, int RB, bool SCHED = false>
+template <typename T, int EPI, int BM, int BN, int WGM, int WGN, int S, int RB, bool SCHED = false,
+          bool EARLY = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch) {
   const GemmArgs& a = launch.a;
   constexpr int NT = 64 * WGM * WGN, NW = WGM * WGN;
@@ -404,6 +405,78 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
       if (kt + 1 < nk) lstore(cur ^ 1);
       __syncthreads();
     }
+  } else if constexpr (EARLY) {
+    // Two stages, direct-to-LDS loads, and the hand-over between them one
+    // k-substep before the end of a k-tile: after the last substep's
+    // operands are in registers, the waves meet, the k-tile after next is
+    // issued into the stage just finished, and the next k-tile's first
+    // operands are read while the last substep's MFMAs run.  The body has
+    // no branch: the final two iterations reload the last k-tile into a
+    // stage nobody reads any more (drained before the epilogue).
+    static_assert(S == 2, "hand-over variant uses two stages");
+    constexpr int RPI = 1024 / RB;
+    constexpr int DPW = ROWS / RPI / NW;
+    static_assert(DPW * RPI * NW == ROWS, "stage rows must split over the waves");
+    const T* src[DPW];
+#pragma unroll
+    for (int d = 0; d < DPW; ++d) {
+      const int r = (wave * DPW + d) * RPI + lane / CPR;
+      const int c = swz<CPR>(lane % CPR, r);
+      src[d] = r < BM ? Pm + (long long)r * a.ldp + c * EPC
+                      : Qm + (long long)(r - BM) * a.ldq + c * EPC;
+    }
+    auto issue = [&](int kt, int stage) {
+#pragma unroll
+      for (int d = 0; d < DPW; ++d)
+        load_lds16(src[d] + (long long)kt * BK,
+                   smem + (size_t)stage * STAGE * 16 + (size_t)(wave * DPW + d) * 1024);
+    };
+    auto mfmas = [&](int slot) {
+#pragma unroll
+      for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < FN; ++ni) mma<T>(acc[mi][ni], fa[slot][mi], fb[slot][ni]);
+    };
+    issue(0, 0);
+    wait_vmcnt<0>();
+    barrier_no_fence();
+    issue(nk > 1 ? 1 : 0, 1);
+    fload(lds, 0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const u32x4_t* L = lds + (kt & 1) * STAGE;
+#pragma unroll
+      for (int kk = 0; kk + 1 < KK; ++kk) {
+        fload(L, kk + 1, (kk + 1) & 1);
+        mfmas(kk & 1);
+      }
+      if constexpr (SCHED) {
+#pragma unroll
+        for (int kk = 0; kk + 1 < KK; ++kk) {
+#pragma unroll
+          for (int x = 0; x < FM + FN; ++x) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
+        }
+      }
+      wait_vmcnt<0>();    // this wave's part of k-tile kt+1 has landed
+      barrier_no_fence();  // everyone's has; everyone is done reading stage kt&1
+      issue(kt + 2 < nk ? kt + 2 : nk - 1, kt & 1);
+      fload(lds + ((kt + 1) & 1) * STAGE, 0, 0);
+      mfmas((KK - 1) & 1);
+      if constexpr (SCHED) {
+        __builtin_amdgcn_sched_group_barrier(0x020, DPW, 0);  // the loads
+#pragma unroll
+        for (int x = 0; x < FM + FN; ++x) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
+      }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
   } else {
     // Direct-to-LDS loads.  One instruction moves 64 x 16 bytes = RPI rows;
     // each wave owns DPW of them per stage.  Lane l fills LDS slot l % CPR of
@@ -618,18 +691,20 @@ int gemm_tile(int compute_bf16, int tile_pref) {
 }
 
 // bf16 256x256 tiles on 8 waves (2x4, 128x64 each).  Main loop, chosen by
-// MUON_WAVE_CFG (a tuning knob; default 4):
+// MUON_WAVE_CFG (a tuning knob; by default 5 for GRAM / POLY, 4 otherwise):
 //   0  register-staged loads, 128-byte rows, two LDS stages
 //   1  direct-to-LDS loads, 64-byte rows, 3 stages
 //   3  as 1 with the MFMA / LDS-read order pinned
 //   4  direct-to-LDS loads, 128-byte rows, 2 stages, order pinned
+//   5  as 4 with the stage hand-over one k-substep before the tile's end
 // 128x128 tiles use 4 waves (64x64 each) and register-staged loads.
-static int wave_cfg() {
+static int wave_cfg(int epi) {
   static const int v = [] {
     const char* e = std::getenv("MUON_WAVE_CFG");
-    return e ? std::atoi(e) : 4;
+    return e ? std::atoi(e) : -1;
   }();
-  return v;
+  if (v >= 0) return v;
+  return epi == EPI_GRAM || epi == EPI_POLY ? 5 : 4;
 }
 
 template <typename T, int E>
@@ -638,7 +713,7 @@ static void launch_gemm_t(int tile, const GemmArgs& a, const WeightTable& t, dim
   const GemmLaunch launch{a, t};
   if constexpr (sizeof(T) == 2) {
     if (tile == 256) {
-      switch (wave_cfg()) {
+      switch (wave_cfg(E)) {
         case 0:
           hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 0, 128>), grid, dim3(512), 0, s,
                              launch);
@@ -650,6 +725,10 @@ static void launch_gemm_t(int tile, const GemmArgs& a, const WeightTable& t, dim
         case 3:
           hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 3, 64, true>), grid, dim3(512), 0,
                              s, launch);
+          return;
+        case 5:
+          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 2, 128, true, true>), grid,
+                             dim3(512), 0, s, launch);
           return;
         default:
           hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 2, 128, true>), grid, dim3(512), 0,
