@@ -57,10 +57,14 @@ int pick_tile(bool cbf16, long long tiles_at_256, int batch) {
   return gemm_tile(cbf16, tiles_at_256 * batch >= 512 ? 256 : 128);
 }
 
-// Workspace regions for `cnt` matrices of oriented shape m x n.
+// Workspace regions for `cnt` matrices of oriented shape m x n (padded
+// M x N), the X state as described for PrepArgs:
+//   bf16: hi plane twice (the update reads one, writes the other), lo plane;
+//   fp32: X, X^T twice (read by the update, written by it).
+// Then A and B (M x M, compute precision), the norm partials and 1/norm.
 struct Layout {
   int m = 0, n = 0, M = 0, N = 0, cnt = 0, nblk = 0;
-  size_t xf = 0, xb = 0, xt0 = 0, xt1 = 0, A = 0, B = 0, part = 0, inv = 0, total = 0;
+  size_t x0 = 0, x1 = 0, x2 = 0, A = 0, B = 0, part = 0, inv = 0, total = 0;
 };
 
 bool make_layout(int cnt, int m, int n, bool cbf16, Layout& L) {
@@ -76,10 +80,9 @@ bool make_layout(int cnt, int m, int n, bool cbf16, Layout& L) {
     off = align_up(off + bytes, kWsAlign);
     return o;
   };
-  L.xf = take((size_t)cnt * MN * 4);
-  L.xb = cbf16 ? take((size_t)cnt * MN * 2) : 0;
-  L.xt0 = take((size_t)cnt * MN * es);
-  L.xt1 = take((size_t)cnt * MN * es);
+  L.x0 = take((size_t)cnt * MN * es);  // bf16: hi 0   fp32: X
+  L.x1 = take((size_t)cnt * MN * es);  // bf16: hi 1   fp32: X^T 0
+  L.x2 = take((size_t)cnt * MN * es);  // bf16: lo     fp32: X^T 1
   L.A = take((size_t)cnt * MM * es);
   L.B = take((size_t)cnt * MM * es);
   L.part = take((size_t)cnt * (size_t)L.nblk * 4);
@@ -158,15 +161,18 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
               float eps, bool cbf16, hipStream_t s) {
   const size_t es = cbf16 ? 2 : 4;
   const long long MN = (long long)L.M * L.N, MM = (long long)L.M * L.M;
-  float* Xf = reinterpret_cast<float*>(ws + L.xf);
-  void* Xb = cbf16 ? static_cast<void*>(ws + L.xb) : nullptr;
-  void* XT[2] = {ws + L.xt0, ws + L.xt1};
+  // bf16: Xh[2] (hi planes), Xl; fp32: Xf, XT[2]
+  void* Xh[2] = {ws + L.x0, ws + L.x1};
+  void* Xl = ws + L.x2;
+  float* Xf = reinterpret_cast<float*>(ws + L.x0);
+  void* XT[2] = {ws + L.x1, ws + L.x2};
   void* A = ws + L.A;
   void* B = ws + L.B;
   float* part = reinterpret_cast<float*>(ws + L.part);
   float* inv = reinterpret_cast<float*>(ws + L.inv);
   const double m = L.m, n = L.n, cnt = c.cnt;
   const double elems = m * n * cnt;
+  const double pmn = cnt * (double)MN, pmm = cnt * (double)MM;  // padded elements
 
   PrepArgs pa{};
   pa.m = L.m; pa.n = L.n; pa.M = L.M; pa.N = L.N;
@@ -174,13 +180,16 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
   pa.tiles_n = L.N / kPrepTile;
   pa.in = c.in; pa.s_in = c.s_in;
   pa.mu = c.mu;
-  pa.Xf = Xf; pa.sXf = MN;
-  pa.Xb = Xb;
-  pa.XT = XT[0]; pa.sXT = MN;
+  pa.sX = MN;
+  if (cbf16) {
+    pa.Xh = Xh[0]; pa.Xl = Xl;
+  } else {
+    pa.Xf = Xf; pa.XT = XT[0]; pa.sXT = MN;
+  }
   pa.partials = part; pa.nblk = L.nblk;
+  // reads g (and momentum r/w); writes X_0: hi + lo, or X + X^T
   const double gsz = c.in_bf16 ? 2 : 4;
-  const double prep_bytes = elems * (gsz + (c.momentum ? 8.0 : 0.0)) +
-                            cnt * (double)MN * (cbf16 ? 8.0 : 8.0);
+  const double prep_bytes = elems * (gsz + (c.momentum ? 8.0 : 0.0)) + pmn * (cbf16 ? 4.0 : 8.0);
   hipError_t err = timed(MUON_K_PREP, L.m, L.n, c.cnt, -1, 0.0, prep_bytes, s, [&] {
     return launch_prep(c.in_bf16, cbf16, c.momentum, pa, c.pt, c.cnt, s);
   });
@@ -194,19 +203,20 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
   const int tile_upd = pick_tile(cbf16, (long long)t256 * (L.N / 256), c.cnt);
   for (int k = 0; k < n_steps; ++k) {
     const bool first = k == 0, last = k == n_steps - 1;
+    const int cur = k & 1;
     GemmArgs g{};
     g.inv = first ? inv : nullptr;
     g.a = coeffs[k].a; g.b = coeffs[k].b; g.c = coeffs[k].c;
     g.m = L.m; g.n = L.n; g.tall_mask = c.tall_mask;
 
-    // A = X X^T (K = N)
-    g.P = cbf16 ? Xb : static_cast<void*>(Xf);
+    // A = X X^T (K = N); bf16 reads the hi plane
+    g.P = cbf16 ? Xh[cur] : static_cast<void*>(Xf);
     g.Q = g.P;
     g.sP = g.sQ = MN; g.ldp = g.ldq = L.N; g.K = L.N;
     g.tiles_m = g.tiles_n = L.M / tile_sym; g.tri = 1;
     g.C = A; g.sC = MM; g.ldc = L.M;
     err = timed(MUON_K_GRAM, L.m, L.n, c.cnt, k, cnt * 2.0 * m * m * n,
-                cnt * ((double)MN * es + (double)MM * es), s,
+                pmn * es + pmm * es, s,
                 [&] { return launch_gemm(cbf16, EPI_GRAM, tile_sym, g, c.wt, c.cnt, s); });
     if (err != hipSuccess) return MUON_ERR_HIP;
 
@@ -215,27 +225,36 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
     g.P = g.Q = A; g.sP = g.sQ = MM; g.ldp = g.ldq = L.M; g.K = L.M;
     g.C = B; g.sC = MM; g.ldc = L.M;
     g.Ain = A; g.sAin = MM;
-    err = timed(MUON_K_POLY, L.m, L.n, c.cnt, k, cnt * 2.0 * m * m * m,
-                cnt * 3.0 * (double)MM * es, s,
+    err = timed(MUON_K_POLY, L.m, L.n, c.cnt, k, cnt * 2.0 * m * m * m, 3.0 * pmm * es, s,
                 [&] { return launch_gemm(cbf16, EPI_POLY, tile_sym, g, c.wt, c.cnt, s); });
     if (err != hipSuccess) return MUON_ERR_HIP;
 
-    // X <- a X + B X  (Q = X^T, K = M)
+    // X <- a X + B X (K = M).  bf16: Q = the hi plane itself, row-major
+    // [k][j]; fp32: Q = X^T.
     g.inv = first ? inv : nullptr;
     g.P = B; g.sP = MM; g.ldp = L.M;
-    g.Q = XT[k & 1]; g.sQ = MN; g.ldq = L.M; g.K = L.M;
+    g.K = L.M;
+    g.sX = MN; g.ldx = L.N;
+    if (cbf16) {
+      g.Q = Xh[cur]; g.sQ = MN; g.ldq = L.N;
+      g.Xh = Xh[cur]; g.Xh_next = Xh[cur ^ 1]; g.Xl = Xl;
+    } else {
+      g.Q = XT[cur]; g.sQ = MN; g.ldq = L.M;
+      g.Xf = Xf;
+      g.XTo = XT[cur ^ 1]; g.sXT = MN; g.ldxt = L.M;
+    }
     g.tri = 0; g.tiles_m = L.M / tile_upd; g.tiles_n = L.N / tile_upd;
-    g.Xf = Xf; g.sXf = MN; g.ldx = L.N;
-    g.Xb = Xb;
-    g.XTo = XT[(k + 1) & 1]; g.sXT = MN; g.ldxt = L.M;
     g.final_mode = last ? c.final_mode : FINAL_NONE;
     g.group_m = group_m();
     g.out = c.out; g.s_out = c.s_out; g.out_bf16 = c.out_bf16;
     g.neg_lr = c.neg_lr;
+    // reads B and the operand X; the epilogue reads X (bf16: hi + lo, fp32:
+    // X) and writes the next X (bf16: hi + lo, fp32: X + X^T), or, on the
+    // last step, reads and writes the weights or writes the output
     const double upd_bytes =
-        cnt * ((double)MM * es + (double)MN * es + (double)MN * 4.0) +
+        pmm * es + pmn * es + pmn * 4.0 +
         (last ? (c.final_mode == FINAL_WEIGHTS ? elems * 8.0 : elems * (c.out_bf16 ? 2.0 : 4.0))
-              : cnt * (double)MN * (4.0 + es + (cbf16 ? 2.0 : 0.0)));
+              : pmn * (cbf16 ? 4.0 : 8.0));
     err = timed(last ? MUON_K_FINAL : MUON_K_UPDATE, L.m, L.n, c.cnt, k, cnt * 2.0 * m * m * n,
                 upd_bytes, s,
                 [&] { return launch_gemm(cbf16, !last ? EPI_UPDATE

@@ -15,14 +15,19 @@ constexpr int kPad = 256;
 constexpr int kPrepTile = 64;
 
 // GEMM epilogues: GRAM A = inv^2 X X^T; POLY B = b A + c A A; UPDATE
-// X <- scl (a X + B X) with X, bf16 X and X^T written; FINAL_W the same
-// value subtracted (times lr * scale) from the weights; FINAL_OUT the same
-// value written to the caller's output.
+// X <- scl (a X + B X) written as the next X state; FINAL_W the same value
+// subtracted (times lr * scale) from the weights; FINAL_OUT the same value
+// written to the caller's output.
 enum Epi { EPI_GRAM = 0, EPI_POLY = 1, EPI_UPDATE = 2, EPI_FINAL_W = 3, EPI_FINAL_OUT = 4 };
 enum Final { FINAL_NONE = 0, FINAL_OUT = 1, FINAL_WEIGHTS = 2 };
 
 // Inputs of the prep kernel: momentum (step) or plain input (orthogonalize),
 // Frobenius partial sums, and the oriented, zero-padded X_0 copies.
+// X state between Newton-Schulz steps, oriented M x N per matrix:
+//   bf16 compute: X = hi + lo, two bf16 planes (hi is also the MFMA operand;
+//                 it is double-buffered because the update reads all of hi
+//                 as its second operand while writing the next hi);
+//   fp32 compute: X in fp32, plus X^T (N x M) as the update's operand.
 struct PrepArgs {
   int m, n, M, N;          // oriented shape and its padded size
   unsigned long long tall_mask;  // bit i: matrix i is tall (rows = n, cols = m),
@@ -31,11 +36,10 @@ struct PrepArgs {
   const void* in;          // orthogonalize: input base (matrix i at in + i*s_in)
   long long s_in;
   float mu;
-  float* Xf;               // fp32 X_0, M x N per matrix
-  long long sXf;
-  void* Xb;                // bf16 X_0, M x N (bf16 compute only)
-  void* XT;                // X_0^T, N x M, compute type
-  long long sXT;
+  long long sX;            // per-matrix stride of the M x N planes
+  void* Xh; void* Xl;      // bf16: hi, lo of X_0
+  float* Xf;               // fp32: X_0
+  void* XT; long long sXT; // fp32: X_0^T, N x M
   float* partials;         // [matrix][tile] sum of u^2
   int nblk;                // tiles per matrix
 };
@@ -46,6 +50,8 @@ struct PrepTable {         // step only: per-matrix gradient / momentum pointers
 };
 
 // C[i][j] = sum_k P[i][k] Q[j][k] over a padded batch, with an epilogue.
+// The bf16 UPDATE / FINAL take Q row-major instead (Q[k][j] at
+// Q + k * ldq + j): their second operand is the hi plane of X itself.
 struct GemmArgs {
   const void* P; const void* Q;
   long long sP, sQ;        // per-matrix strides, elements
@@ -59,10 +65,11 @@ struct GemmArgs {
   // GRAM / POLY output (M x M), POLY input A
   void* C; long long sC; int ldc;
   const void* Ain; long long sAin;
-  // UPDATE
-  float* Xf; long long sXf; int ldx;     // fp32 X, read a*X, write X_{k+1}
-  void* Xb;                              // bf16 X copy (bf16 compute)
-  void* XTo; long long sXT; int ldxt;    // X_{k+1}^T for the next step
+  // UPDATE / FINAL: X state (see PrepArgs), leading dimension ldx, stride sX
+  long long sX; int ldx;
+  const void* Xh; void* Xh_next; void* Xl;  // bf16: hi (read), next hi, lo (in place)
+  float* Xf;                                 // fp32: X (in place)
+  void* XTo; long long sXT; int ldxt;        // fp32: next step's X^T
   int m, n;
   unsigned long long tall_mask;          // bit i: matrix i is stored tall
   int final_mode;

@@ -8,13 +8,15 @@
 // Kernels (one launch each per oriented shape group and step):
 //   prep_kernel    momentum + Frobenius partial sums + oriented, zero-padded X_0
 //   norm_kernel    fixed-order reduction of the partials -> 1/(||u||_F + eps)
-//   gemm_kernel    C[i][j] = sum_k P[i][k] Q[j][k] on MFMA, three epilogues:
+//   gemm_kernel    C[i][j] = sum_k P[i][k] Q[j][k] on MFMA, epilogues:
 //                    GRAM   A = X X^T        (lower-triangle tiles, mirrored)
 //                    POLY   B = b A + c A A  (A symmetric, so A A = A A^T)
-//                    UPDATE X <- a X + B X   (Q = X^T, kept as its own copy)
+//                    UPDATE X <- a X + B X   (bf16: Q is X's hi plane, read
+//                                             row-major and transposed in LDS;
+//                                             fp32: Q = X^T, kept as a copy)
+//                    FINAL  the last UPDATE, into the weights or the output
 // The 1/||u|| normalisation is folded into the first GRAM (x inv^2) and
-// UPDATE (x inv) epilogues; the last UPDATE writes the weights (or the
-// output) in the caller's orientation.
+// UPDATE (x inv) epilogues.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -30,6 +32,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 // Kernel arguments are read in place from the kernarg segment: indexing a
 // per-matrix table with the matrix index must not copy the table to scratch.
@@ -50,6 +54,13 @@ __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
   return static_cast<bf16_t>(x);  // v_cvt_pk_bf16_f32: round to nearest even
 }
 
+// x as the sum of two bf16 values: hi = bf16(x), lo = bf16(x - hi) (the
+// difference is exact in fp32), 16 significant bits in all.
+__device__ __forceinline__ void split_bf16(float x, bf16_t& hi, bf16_t& lo) {
+  hi = from_f32<bf16_t>(x);
+  lo = from_f32<bf16_t>(x - to_f32(hi));
+}
+
 // Compile-time loop: f(std::integral_constant<int, 0>) ... f(<N-1>), so that
 // register arrays are never indexed at run time (which would put them in
 // scratch memory).
@@ -64,13 +75,16 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 // ---------------------------------------------------------------- prep
 // One 64x64 tile of the oriented, padded M x N space per block.  Reads the
-// original matrix coalesced along its rows, writes the copy that shares the
-// original layout directly and the transposed copy through an LDS tile.
+// original matrix coalesced along its rows; outputs that share the original
+// layout are written directly, the others through a transposing LDS tile.
+//   CT = bf16: X_0 as its hi and lo planes (M x N);
+//   CT = fp32: X_0 (M x N) and X_0^T (N x M).
 template <typename GT, typename CT, bool MOM>
 __global__ __launch_bounds__(256) void prep_kernel(PrepLaunch launch) {
   const PrepArgs& a = launch.a;
   __shared__ float tile[kPrepTile][kPrepTile + 1];
   __shared__ float red[4];
+  constexpr bool HILO = sizeof(CT) == 2;
   const int tid = threadIdx.x;
   const int mat = blockIdx.y;
   const int bt = blockIdx.x;
@@ -89,9 +103,27 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepLaunch launch) {
   } else {
     g = static_cast<const GT*>(a.in) + (long long)mat * a.s_in;
   }
-  float* Xf = a.Xf + (long long)mat * a.sXf;
-  bf16_t* Xb = a.Xb ? static_cast<bf16_t*>(a.Xb) + (long long)mat * a.sXf : nullptr;
-  CT* XT = static_cast<CT*>(a.XT) + (long long)mat * a.sXT;
+  bf16_t* Xh = nullptr;
+  bf16_t* Xl = nullptr;
+  float* Xf = nullptr;
+  float* XT = nullptr;
+  if constexpr (HILO) {
+    Xh = static_cast<bf16_t*>(a.Xh) + (long long)mat * a.sX;
+    Xl = static_cast<bf16_t*>(a.Xl) + (long long)mat * a.sX;
+  } else {
+    Xf = a.Xf + (long long)mat * a.sX;
+    XT = static_cast<float*>(a.XT) + (long long)mat * a.sXT;
+  }
+  auto put_x = [&](long long o, float u) {  // X[oi][oj] at offset o
+    if constexpr (HILO) {
+      bf16_t hi, lo;
+      split_bf16(u, hi, lo);
+      Xh[o] = hi;
+      Xl[o] = lo;
+    } else {
+      Xf[o] = u;
+    }
+  };
 
   const int cc = tid & 63, rr = tid >> 6;
   float sum = 0.f;
@@ -112,12 +144,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepLaunch launch) {
       }
     }
     sum += u * u;
-    if (!tall) {  // X[oi][oj] = X[r][c]
-      const long long o = (long long)r * a.N + c;
-      Xf[o] = u;
-      if (Xb) Xb[o] = from_f32<bf16_t>(u);
-    } else {        // X^T[oj][oi] = X^T[r][c]
-      XT[(long long)r * a.M + c] = from_f32<CT>(u);
+    if (!tall) {
+      put_x((long long)r * a.N + c, u);  // X[oi][oj] = X[r][c]
+    } else if constexpr (!HILO) {
+      XT[(long long)r * a.M + c] = u;    // X^T[oj][oi] = X^T[r][c]
     }
     tile[lr][cc] = u;
   }
@@ -127,12 +157,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepLaunch launch) {
     const int lc = rr + 4 * p;
     const float u = tile[cc][lc];
     const int r = r0 + cc, c = c0 + lc;
-    if (!tall) {  // X^T[oj][oi] = X^T[c][r]
-      XT[(long long)c * a.M + r] = from_f32<CT>(u);
-    } else {        // X[oi][oj] = X[c][r]
-      const long long o = (long long)c * a.N + r;
-      Xf[o] = u;
-      if (Xb) Xb[o] = from_f32<bf16_t>(u);
+    if (tall) {
+      put_x((long long)c * a.N + r, u);  // X[oi][oj] = X[c][r]
+    } else if constexpr (!HILO) {
+      XT[(long long)c * a.M + r] = u;    // X^T[oj][oi] = X^T[c][r]
     }
   }
   // Deterministic block sum: wave butterfly, then the four waves in order.
@@ -199,16 +227,22 @@ __device__ __forceinline__ void decode_tile(const GemmArgs& a, int& mat, int& ti
   }
 }
 
-// LDS slot of 16-byte chunk `c` of tile row `r`, rows of CPR chunks.  The
-// LDS has 64 four-byte banks (256 bytes) and serves 16 lanes of a 16-byte
-// access per cycle; 256 / (16 CPR) rows share one bank line, so the chunk
-// order is permuted by the index of the row's bank line: 16 consecutive rows
-// at one chunk then hit 16 distinct bank groups (MFMA operand reads), and the
-// CPR lanes writing one row stay distinct (loader stores).
-template <int CPR>
-__device__ __forceinline__ int swz(int c, int r) {
-  constexpr int RPL = 16 / CPR;  // rows per 256-byte bank line
-  return c ^ ((r / RPL) % CPR);
+// LDS slot of 16-byte chunk `c` of a 128-byte operand row `r`.  The LDS has
+// 64 four-byte banks (256 bytes per bank line) and serves 16 lanes of a
+// 16-byte access per cycle; two rows share a bank line, so the chunk order
+// is permuted by the row pair index: 16 consecutive rows at one chunk hit 16
+// distinct bank groups (MFMA operand reads), and the 8 lanes filling one row
+// stay distinct.  An involution: slot s of row r holds chunk swz(s, r).
+__device__ __forceinline__ int swz(int c, int r) { return c ^ ((r >> 1) & 7); }
+
+// Row-major [k][j] operand tile (bf16 UPDATE's X), k-rows of SEGS 64-byte
+// segments (4 chunks each): the segment order of k-row k is permuted by
+// k % SEGS.  A transposing read touches 4 consecutive k-rows at one logical
+// segment per 32 lanes, which then fall on 4 distinct quarters of the bank
+// line.  Also an involution, in the chunk index u.
+template <int SEGS>
+__device__ __forceinline__ int qrow_unit(int k, int u) {
+  return (((u >> 2) ^ (k % SEGS)) << 2) | (u & 3);
 }
 
 template <typename T>
@@ -230,19 +264,6 @@ __device__ __forceinline__ void mma<float>(f32x16_t& acc, const u32x4_t& fa, con
   for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[e], bv[e], acc, 0, 0, 0);
 }
 
-// Block tile BM x BN computed by WGM x WGN waves, each owning a
-// (BM/WGM) x (BN/WGN) sub-tile of 32x32 MFMA tiles.  K advances 128 bytes
-// per row (64 bf16 or 32 fp32) per step through two LDS stages; a row's
-// 16-byte chunks are permuted (swz) so that both the stores of the loader
-// and the operand reads of the MFMA lanes are free of bank conflicts.  Operand fragments are double-buffered in registers.
-//
-// Epilogue, one 32-row block of the wave tile at a time: first all of its
-// inputs are loaded (C/X values the epilogue combines with), then values
-// are computed and stored.  The accumulators hold, per lane, 4 consecutive
-// rows i of one column j, so row-major C[i][j] outputs are stored directly
-// (consecutive lanes -> consecutive j).  Transposed outputs (the mirrored
-// triangle of A and B, the next step's X^T) are staged in LDS as [j][i]
-// rows and stored as coalesced 16-byte chunks.
 // Wait until at most N vector-memory operations of this wave are in flight
 // (other counters untouched): s_waitcnt with vmcnt = N, expcnt = 7,
 // lgkmcnt = 15.
@@ -276,35 +297,89 @@ __device__ __forceinline__ void load_lds16(const void* src, void* lds_wave_base)
 #endif
 }
 
-// Main loop variants (template parameter S):
-//  S == 0  operands go global -> registers -> LDS, two LDS stages, the next
-//          k-tile's loads in flight while the current one is multiplied;
-//  S >= 2  operands go global -> LDS directly (global_load_lds_dwordx4:
-//          lane l of a wave writes 16 bytes at the wave's LDS address + 16 l),
-//          S LDS stages, loads issued S - 1 k-tiles ahead.
-// RB is the bytes of one operand row per k-tile (64 or 128).
-template <typename T, int EPI, int BM, int BN, int WGM, int WGN, int S, int RB, bool SCHED = false,
-          bool EARLY = false>
+// Transposing LDS read of 4 x 16 bits (ds_read_b64_tr_b16), 8-byte aligned
+// addresses.  In each group of 16 lanes, lane i receives element i % 4 of
+// the 8-byte rows addressed by lanes i/4, i/4 + 4, i/4 + 8 and i/4 + 12, in
+// that order.
+__device__ __forceinline__ u32x2_t lds_read_tr16(const void* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4_t*)(p));
+  return __builtin_bit_cast(u32x2_t, v);
+#else
+  return u32x2_t{0u, 0u};
+#endif
+}
+
+// Block tile BM x BN computed by WGM x WGN waves, each owning a
+// (BM/WGM) x (BN/WGN) sub-tile of 32x32 MFMA tiles, fp32 accumulators.  K
+// advances 128 bytes per operand row (64 bf16 or 32 fp32) per k-tile.
+//
+// A stage holds the k-tile of both operands in 16-byte chunks: BM rows of P
+// (8 chunks each, swz), then Q's BN rows (8 chunks each, swz) or, with QROW,
+// Q's row-major k-tile: BK k-rows of BN / 8 chunks (qrow_unit), read with
+// the transposing LDS read, which hands each lane 4 k-values of its column.
+//
+// Main loop (S):
+//   S == 0  global -> registers -> LDS, two stages, the next k-tile's loads in
+//           flight while the current one is multiplied;
+//   S == 2  global -> LDS directly (global_load_lds_dwordx4), two stages, an
+//           explicit vmcnt wait and a fence-free barrier per k-tile; EARLY
+//           moves the hand-over one k-substep before the k-tile's end.
+// SCHED pins the order of MFMAs and operand reads: each later k-substep's
+// reads go one after each MFMA of the substep before it.
+//
+// Epilogue, one 32-row block of the wave tile at a time: inputs loaded first,
+// then values computed and stored.  The accumulators hold, per lane, 4
+// consecutive rows i of one column j, so row-major outputs are stored
+// directly (consecutive lanes -> consecutive j); transposed outputs (the
+// mirrored triangle of A and B, the fp32 path's X^T) are staged in LDS as
+// [j][i] rows and stored as coalesced 16-byte chunks.
+template <typename T, int EPI, int BM, int BN, int WGM, int WGN, int S, bool SCHED, bool EARLY,
+          bool QROW>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch) {
   const GemmArgs& a = launch.a;
   constexpr int NT = 64 * WGM * WGN, NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
-  constexpr int CPR = RB / 16;              // chunks per operand row and k-tile
+  constexpr int CPR = 8;                    // chunks per operand row and k-tile
   constexpr int BK = CPR * EPC;             // k per k-tile
-  constexpr int KK = CPR / 2;               // MFMA k-substeps per k-tile
-  constexpr int ROWS = BM + BN;             // P rows, then Q rows
-  constexpr int STAGE = ROWS * CPR;         // 16-byte chunks per stage
-  constexpr int NSTAGE = S == 0 ? 2 : S;
-  constexpr int TLD = BM + 8;               // row stride of the transposed tile
-  constexpr size_t MAIN_BYTES = (size_t)NSTAGE * STAGE * 16;
+  constexpr int KK = 4;                     // MFMA k-substeps per k-tile
+  constexpr int P_CHUNKS = BM * CPR;
+  constexpr int STAGE = P_CHUNKS + BN * CPR;  // with QROW: BK * (BN / 8), the same
+  constexpr int UPR = BN / 8;                 // QROW: chunks per k-row
+  constexpr int SEGS = BN / 32;               // QROW: 64-byte segments per k-row
+  constexpr int TLD = BM + 8;                 // row stride of the transposed tile
+  constexpr size_t MAIN_BYTES = 2 * (size_t)STAGE * 16;
   constexpr size_t EPI_BYTES = (size_t)BN * TLD * sizeof(T);
   constexpr size_t LDS_BYTES = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
+  constexpr bool FINAL = EPI == EPI_FINAL_W || EPI == EPI_FINAL_OUT;
+  constexpr bool HILO = sizeof(T) == 2;  // bf16 path: X state as hi + lo planes
+  constexpr bool STAGED_T = EPI == EPI_GRAM || EPI == EPI_POLY || (EPI == EPI_UPDATE && !HILO);
   static_assert(FM * 32 * WGM == BM && FN * 32 * WGN == BN, "wave tiles must be 32-aligned");
-  static_assert(S == 0 ? RB == 128 : S >= 2, "register path uses 128-byte rows");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
-  u32x4_t* lds = reinterpret_cast<u32x4_t*>(smem);
+  static_assert(S == 0 || S == 2, "main loop variants");
+  static_assert(!QROW || (HILO && BK == 64 && !STAGED_T), "row-major Q is the bf16 X operand");
+  // The two stages.  With QROW they are two distinct LDS objects: the
+  // compiler's wait analysis then sees that the transposing reads of one
+  // stage do not alias the direct-to-LDS loads in flight into the other
+  // (with one object it waits for every load before each such read).  The
+  // QROW epilogues stage nothing in LDS.  Otherwise one object holds both
+  // stages and, in the epilogue, the transposed tile.
+  u32x4_t* S0;
+  u32x4_t* S1;
+  unsigned char* smem;
+  if constexpr (QROW) {
+    __shared__ u32x4_t stage0[STAGE], stage1[STAGE];
+    S0 = stage0;
+    S1 = stage1;
+    smem = nullptr;
+  } else {
+    __shared__ __attribute__((aligned(16))) unsigned char lds_all[LDS_BYTES];
+    smem = lds_all;
+    S0 = reinterpret_cast<u32x4_t*>(lds_all);
+    S1 = S0 + STAGE;
+  }
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
@@ -312,9 +387,29 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
   decode_tile(a, mat, ti, tj);
   const T* __restrict__ Pm =
       static_cast<const T*>(a.P) + (long long)mat * a.sP + (long long)ti * BM * a.ldp;
+  // Q's tile: BN rows from row tj * BN, or (QROW) BN columns from column tj * BN
   const T* __restrict__ Qm =
-      static_cast<const T*>(a.Q) + (long long)mat * a.sQ + (long long)tj * BN * a.ldq;
+      QROW ? static_cast<const T*>(a.Q) + (long long)mat * a.sQ + (long long)tj * BN
+           : static_cast<const T*>(a.Q) + (long long)mat * a.sQ + (long long)tj * BN * a.ldq;
   const int nk = a.K / BK;
+  // Advance of a Q chunk's source per k-tile, in elements (P's is BK).
+  const long long qstep = QROW ? (long long)BK * a.ldq : BK;
+
+  // Global source, at k-tile 0, of the chunk that fills LDS chunk q of a stage.
+  auto chunk_src = [&](int q) -> const T* {
+    if (q < P_CHUNKS) {
+      const int r = q / CPR;
+      return Pm + (long long)r * a.ldp + swz(q % CPR, r) * EPC;
+    }
+    const int qq = q - P_CHUNKS;
+    if constexpr (QROW) {
+      const int k = qq / UPR;
+      return Qm + (long long)k * a.ldq + qrow_unit<SEGS>(k, qq % UPR) * EPC;
+    } else {
+      const int r = qq / CPR;
+      return Qm + (long long)r * a.ldq + swz(qq % CPR, BM + r) * EPC;
+    }
+  };
 
   f32x16_t acc[FM][FN];
 #pragma unroll
@@ -326,18 +421,65 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
 
   const int arow = wm * WTM + (lane & 31), brow = BM + wn * WTN + (lane & 31);
   const int hsel = lane >> 5;
+  // QROW operand reads: lane c of a 16-lane group addresses k-row
+  // 16 kk + 8 hsel + 4 h + c / 4 and columns j .. j + 3, j = 16 g + 4 (c % 4)
+  // within its 32-column block (g = the group's position in its half-wave),
+  // so lane (32 hsel + 16 g + c) receives column 16 g + c, k = 8 hsel + 4 h + e.
+  const int tr_k = 8 * hsel + ((lane & 15) >> 2);
+  const int tr_j = wn * WTN + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   u32x4_t fa[2][FM], fb[2][FN];
+  // Operand reads of k-substep kk in the order the MFMAs (mi-major) first
+  // use them: A row block 0, every B column block, then the other A blocks.
   auto fload = [&](const u32x4_t* L, int kk, int slot) {
     const int ch = 2 * kk + hsel;
-#pragma unroll
-    for (int mi = 0; mi < FM; ++mi) {
+    auto read_a = [&](int mi) {
       const int r = arow + mi * 32;
-      fa[slot][mi] = L[r * CPR + swz<CPR>(ch, r)];
-    }
+      fa[slot][mi] = L[r * CPR + swz(ch, r)];
+    };
+    read_a(0);
 #pragma unroll
     for (int ni = 0; ni < FN; ++ni) {
-      const int r = brow + ni * 32;
-      fb[slot][ni] = L[r * CPR + swz<CPR>(ch, r)];
+      if constexpr (QROW) {
+        const unsigned char* Lq = reinterpret_cast<const unsigned char*>(L + P_CHUNKS);
+        const int j = tr_j + ni * 32;
+        u32x2_t half[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int k = 16 * kk + tr_k + 4 * h;
+          half[h] = lds_read_tr16(Lq + (k * UPR + qrow_unit<SEGS>(k, j >> 3)) * 16 + (j & 7) * 2);
+        }
+        fb[slot][ni] = u32x4_t{half[0][0], half[0][1], half[1][0], half[1][1]};
+      } else {
+        const int r = brow + ni * 32;
+        fb[slot][ni] = L[r * CPR + swz(ch, r)];
+      }
+    }
+#pragma unroll
+    for (int mi = 1; mi < FM; ++mi) read_a(mi);
+  };
+  auto mfmas = [&](int slot) {
+#pragma unroll
+    for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < FN; ++ni) mma<T>(acc[mi][ni], fa[slot][mi], fb[slot][ni]);
+  };
+  // LDS reads per k-substep, and the pinned order for n substeps: each
+  // MFMA followed by one read of the next substep's operands.
+  constexpr int NREAD = FM + (QROW ? 2 * FN : FN);
+  constexpr int NPAIR = NREAD < FM * FN ? NREAD : FM * FN;
+  auto schedule_substeps = [&](int n) {
+    if constexpr (SCHED) {
+      for (int kk = 0; kk < n; ++kk) {
+#pragma unroll
+        for (int x = 0; x < NPAIR; ++x) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        }
+        if constexpr (FM * FN > NPAIR)
+          __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - NPAIR, 0);
+        if constexpr (NREAD > NPAIR)
+          __builtin_amdgcn_sched_group_barrier(0x100, NREAD - NPAIR, 0);
+      }
     }
   };
   auto compute = [&](const u32x4_t* L) {
@@ -345,187 +487,118 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       if (kk + 1 < KK) fload(L, kk + 1, (kk + 1) & 1);
-#pragma unroll
-      for (int mi = 0; mi < FM; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < FN; ++ni) mma<T>(acc[mi][ni], fa[kk & 1][mi], fb[kk & 1][ni]);
+      mfmas(kk & 1);
     }
-    if constexpr (S >= 2 && SCHED) {
-      // Pinned order: the first substep's reads, then each later substep's
-      // reads one after each MFMA of the substep before it.
-      __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
-#pragma unroll
-      for (int kk = 0; kk + 1 < KK; ++kk) {
-#pragma unroll
-        for (int x = 0; x < FM + FN; ++x) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
-      }
+    if constexpr (SCHED) {
+      __builtin_amdgcn_sched_group_barrier(0x100, NREAD, 0);
+      schedule_substeps(KK - 1);
       __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
     }
   };
 
+  // nk is even (K is a multiple of 256), so the k-loops below go two
+  // k-tiles per iteration, stage S0 then stage S1, both fixed at compile time.
   if constexpr (S == 0) {
-    constexpr int RPP = NT / 8;  // rows per loader pass
-    constexpr int PA = BM / RPP, PB = BN / RPP;
-    static_assert(PA * RPP == BM && PB * RPP == BN, "tile rows must split over the loader");
-    const int lch = tid & 7, lrow = tid >> 3;
-    u32x4_t rp[PA], rq[PB];
+    // Thread t moves LDS chunks t + NT i of each stage.
+    constexpr int PER = STAGE / NT;
+    static_assert(PER * NT == STAGE && P_CHUNKS % NT == 0, "stage chunks must split over the threads");
+    const T* src[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) src[i] = chunk_src(tid + NT * i);
+    u32x4_t rg[PER];
     auto gload = [&](int kt) {
-      const int kofs = kt * BK + lch * EPC;
 #pragma unroll
-      for (int s = 0; s < PA; ++s)
-        rp[s] = *reinterpret_cast<const u32x4_t*>(Pm + (long long)(lrow + RPP * s) * a.ldp + kofs);
-#pragma unroll
-      for (int s = 0; s < PB; ++s)
-        rq[s] = *reinterpret_cast<const u32x4_t*>(Qm + (long long)(lrow + RPP * s) * a.ldq + kofs);
+      for (int i = 0; i < PER; ++i) {
+        const long long step = i < P_CHUNKS / NT ? (long long)BK : qstep;
+        rg[i] = *reinterpret_cast<const u32x4_t*>(src[i] + kt * step);
+      }
     };
-    auto lstore = [&](int b) {
-      u32x4_t* L = lds + b * STAGE;
+    auto lstore = [&](u32x4_t* St) {
 #pragma unroll
-      for (int s = 0; s < PA; ++s) {
-        const int r = lrow + RPP * s;
-        L[r * 8 + swz<8>(lch, r)] = rp[s];
-      }
-#pragma unroll
-      for (int s = 0; s < PB; ++s) {
-        const int r = BM + lrow + RPP * s;
-        L[r * 8 + swz<8>(lch, r)] = rq[s];
-      }
+      for (int i = 0; i < PER; ++i) St[tid + NT * i] = rg[i];
+    };
+    auto ktile = [&](int kt, const u32x4_t* cur, u32x4_t* nxt) {
+      if (kt + 1 < nk) gload(kt + 1);
+      compute(cur);
+      if (kt + 1 < nk) lstore(nxt);
+      __syncthreads();
     };
     gload(0);
-    lstore(0);
+    lstore(S0);
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < nk) gload(kt + 1);
-      compute(lds + cur * STAGE);
-      if (kt + 1 < nk) lstore(cur ^ 1);
-      __syncthreads();
+    for (int kt = 0; kt < nk; kt += 2) {
+      ktile(kt, S0, S1);
+      ktile(kt + 1, S1, S0);
     }
-  } else if constexpr (EARLY) {
-    // Two stages, direct-to-LDS loads, and the hand-over between them one
-    // k-substep before the end of a k-tile: after the last substep's
-    // operands are in registers, the waves meet, the k-tile after next is
-    // issued into the stage just finished, and the next k-tile's first
-    // operands are read while the last substep's MFMAs run.  The body has
-    // no branch: the final two iterations reload the last k-tile into a
-    // stage nobody reads any more (drained before the epilogue).
-    static_assert(S == 2, "hand-over variant uses two stages");
-    constexpr int RPI = 1024 / RB;
-    constexpr int DPW = ROWS / RPI / NW;
-    static_assert(DPW * RPI * NW == ROWS, "stage rows must split over the waves");
+  } else {
+    // Direct-to-LDS loads: instruction d of wave w moves LDS chunks
+    // 64 g .. 64 g + 63 of a stage, g = w DPW + d (lane l: chunk 64 g + l).
+    // A wave's chunks all belong to one operand, so its k-tile advance is
+    // one wave-uniform value.
+    constexpr int DPW = STAGE / 64 / NW;
+    static_assert(DPW * 64 * NW == STAGE && P_CHUNKS % (DPW * 64) == 0,
+                  "stage chunks must split over the waves, one operand per wave");
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    const long long kstep = wave_s * DPW * 64 < P_CHUNKS ? (long long)BK : qstep;
     const T* src[DPW];
 #pragma unroll
-    for (int d = 0; d < DPW; ++d) {
-      const int r = (wave * DPW + d) * RPI + lane / CPR;
-      const int c = swz<CPR>(lane % CPR, r);
-      src[d] = r < BM ? Pm + (long long)r * a.ldp + c * EPC
-                      : Qm + (long long)(r - BM) * a.ldq + c * EPC;
-    }
-    auto issue = [&](int kt, int stage) {
+    for (int d = 0; d < DPW; ++d) src[d] = chunk_src((wave * DPW + d) * 64 + lane);
+    auto issue = [&](int kt, u32x4_t* St) {
+      const long long off = kt * kstep;
 #pragma unroll
-      for (int d = 0; d < DPW; ++d)
-        load_lds16(src[d] + (long long)kt * BK,
-                   smem + (size_t)stage * STAGE * 16 + (size_t)(wave * DPW + d) * 1024);
+      for (int d = 0; d < DPW; ++d) load_lds16(src[d] + off, St + (wave_s * DPW + d) * 64);
     };
-    auto mfmas = [&](int slot) {
-#pragma unroll
-      for (int mi = 0; mi < FM; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < FN; ++ni) mma<T>(acc[mi][ni], fa[slot][mi], fb[slot][ni]);
-    };
-    issue(0, 0);
-    wait_vmcnt<0>();
-    barrier_no_fence();
-    issue(nk > 1 ? 1 : 0, 1);
-    fload(lds, 0, 0);
-    for (int kt = 0; kt < nk; ++kt) {
-      const u32x4_t* L = lds + (kt & 1) * STAGE;
-#pragma unroll
-      for (int kk = 0; kk + 1 < KK; ++kk) {
-        fload(L, kk + 1, (kk + 1) & 1);
-        mfmas(kk & 1);
+    if constexpr (!EARLY) {
+      auto ktile = [&](int kt, const u32x4_t* cur, u32x4_t* nxt) {
+        wait_vmcnt<0>();     // this wave's part of k-tile kt has landed
+        barrier_no_fence();  // everyone's has; everyone is done reading nxt
+        if (kt + 1 < nk) issue(kt + 1, nxt);
+        compute(cur);
+      };
+      issue(0, S0);
+      for (int kt = 0; kt < nk; kt += 2) {
+        ktile(kt, S0, S1);
+        ktile(kt + 1, S1, S0);
       }
-      if constexpr (SCHED) {
+      __syncthreads();
+    } else {
+      // The waves meet once the last k-substep's operands are in registers;
+      // the k-tile after next then goes into the stage just finished, and the
+      // next k-tile's first operands are read while the last substep's MFMAs
+      // run.  No branch in the body: the final two k-tiles reload the last
+      // k-tile into a stage nobody reads any more (drained below).
+      auto ktile = [&](int kt, u32x4_t* cur, const u32x4_t* nxt) {
 #pragma unroll
         for (int kk = 0; kk + 1 < KK; ++kk) {
-#pragma unroll
-          for (int x = 0; x < FM + FN; ++x) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
+          fload(cur, kk + 1, (kk + 1) & 1);
+          mfmas(kk & 1);
         }
+        schedule_substeps(KK - 1);
+        wait_vmcnt<0>();     // this wave's part of k-tile kt+1 has landed
+        barrier_no_fence();  // everyone's has; everyone is done reading cur
+        issue(kt + 2 < nk ? kt + 2 : nk - 1, cur);
+        fload(nxt, 0, 0);
+        mfmas((KK - 1) & 1);
+        if constexpr (SCHED) {
+          __builtin_amdgcn_sched_group_barrier(0x020, DPW, 0);  // the loads
+          schedule_substeps(1);
+        }
+      };
+      issue(0, S0);
+      wait_vmcnt<0>();
+      barrier_no_fence();
+      issue(nk > 1 ? 1 : 0, S1);
+      fload(S0, 0, 0);
+      for (int kt = 0; kt < nk; kt += 2) {
+        ktile(kt, S0, S1);
+        ktile(kt + 1, S1, S0);
       }
-      wait_vmcnt<0>();    // this wave's part of k-tile kt+1 has landed
-      barrier_no_fence();  // everyone's has; everyone is done reading stage kt&1
-      issue(kt + 2 < nk ? kt + 2 : nk - 1, kt & 1);
-      fload(lds + ((kt + 1) & 1) * STAGE, 0, 0);
-      mfmas((KK - 1) & 1);
-      if constexpr (SCHED) {
-        __builtin_amdgcn_sched_group_barrier(0x020, DPW, 0);  // the loads
-#pragma unroll
-        for (int x = 0; x < FM + FN; ++x) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
-      }
+      wait_vmcnt<0>();
+      __syncthreads();
     }
-    wait_vmcnt<0>();
-    __syncthreads();
-  } else {
-    // Direct-to-LDS loads.  One instruction moves 64 x 16 bytes = RPI rows;
-    // each wave owns DPW of them per stage.  Lane l fills LDS slot l % CPR of
-    // row l / CPR, so it fetches the global chunk that the swizzle puts there.
-    constexpr int RPI = 1024 / RB;
-    constexpr int DPW = ROWS / RPI / NW;
-    static_assert(DPW * RPI * NW == ROWS, "stage rows must split over the waves");
-    static_assert(DPW * (S - 2) < 64, "vmcnt range");
-    const T* src[DPW];
-#pragma unroll
-    for (int d = 0; d < DPW; ++d) {
-      const int r = (wave * DPW + d) * RPI + lane / CPR;
-      const int c = swz<CPR>(lane % CPR, r);
-      src[d] = r < BM ? Pm + (long long)r * a.ldp + c * EPC
-                      : Qm + (long long)(r - BM) * a.ldq + c * EPC;
-    }
-    auto issue = [&](int kt, int stage) {
-#pragma unroll
-      for (int d = 0; d < DPW; ++d)
-        load_lds16(src[d] + (long long)kt * BK,
-                   smem + (size_t)stage * STAGE * 16 + (size_t)(wave * DPW + d) * 1024);
-    };
-#pragma unroll
-    for (int t = 0; t < S - 1; ++t)
-      if (t < nk) issue(t, t);
-    for (int kt0 = 0; kt0 < nk; kt0 += S) {
-      static_for<S>([&](auto st) {
-        const int kt = kt0 + st;
-        if (kt < nk) {
-          // this wave's loads of k-tile kt have landed once at most
-          // min(S - 2, k-tiles issued after it) load groups are in flight
-          const int later = nk - 1 - kt;
-          if (later >= S - 2) {
-            wait_vmcnt<DPW * (S - 2)>();
-          } else {
-            static_for<S - 2>([&](auto q) {
-              if (later == q) wait_vmcnt<DPW * q>();
-            });
-          }
-          barrier_no_fence();  // every wave's loads of kt are in LDS; stage kt-1 is free
-          if (kt + S - 1 < nk) issue(kt + S - 1, (st + S - 1) % S);
-          compute(lds + st * STAGE);
-        }
-      });
-    }
-    __syncthreads();
   }
 
-  // ---- epilogue (LDS is free: the last iteration ended with a barrier)
+  // ---- epilogue (LDS is free: the main loop ended with a barrier)
   const int i_base = ti * BM + wm * WTM, j_base = tj * BN + wn * WTN;
   float alpha = 1.f, scl = 1.f;
   if (a.inv) {
@@ -535,21 +608,28 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
   }
   const bool tall = (a.tall_mask >> mat) & 1ull;
   // Transposed output of this block: the mirrored tile (GRAM, POLY off the
-  // diagonal) or the next step's X^T (UPDATE).
-  constexpr bool FINAL = EPI == EPI_FINAL_W || EPI == EPI_FINAL_OUT;
+  // diagonal) or, on the fp32 path, the next step's X^T (UPDATE).
   bool stage_t = false;
-  if constexpr (EPI == EPI_UPDATE) stage_t = true;
+  if constexpr (EPI == EPI_UPDATE) stage_t = STAGED_T;
   if constexpr (EPI == EPI_GRAM || EPI == EPI_POLY) stage_t = ti != tj;
   T* __restrict__ Ts = reinterpret_cast<T*>(smem);
   T* __restrict__ C = nullptr;
   const T* __restrict__ Ain = nullptr;
   float* __restrict__ Xf = nullptr;
-  bf16_t* __restrict__ Xb = nullptr;
+  const bf16_t* __restrict__ Xh = nullptr;
+  bf16_t* __restrict__ Xh_next = nullptr;
+  bf16_t* __restrict__ Xl = nullptr;
   float* __restrict__ W = nullptr;
   float wscale = 0.f;
   if constexpr (EPI == EPI_UPDATE || FINAL) {
-    Xf = a.Xf + (long long)mat * a.sXf;
-    if (a.Xb) Xb = static_cast<bf16_t*>(a.Xb) + (long long)mat * a.sXf;
+    if constexpr (HILO) {
+      Xh = static_cast<const bf16_t*>(a.Xh) + (long long)mat * a.sX;
+      Xl = static_cast<bf16_t*>(a.Xl) + (long long)mat * a.sX;
+      if constexpr (EPI == EPI_UPDATE)
+        Xh_next = static_cast<bf16_t*>(a.Xh_next) + (long long)mat * a.sX;
+    } else {
+      Xf = a.Xf + (long long)mat * a.sX;
+    }
     if constexpr (EPI == EPI_FINAL_W) {
       W = kernarg<GemmLaunch>().wt.w[mat];
       wscale = a.neg_lr * kernarg<GemmLaunch>().wt.scale[mat];
@@ -560,51 +640,74 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
   }
   const int jl0 = wn * WTN + (lane & 31);
 
-  static_for<FM>([&](auto mi) {
+  // Epilogue passes: EPN accumulator column blocks and EPQ of the 4 row
+  // quads of one 32-row block at a time (FINAL_W has a third input, so its
+  // passes are smaller to keep the loads in flight within the registers).
+  constexpr int EPN = EPI == EPI_FINAL_W ? 1 : FN;
+  constexpr int EPQ = EPI == EPI_FINAL_W ? 2 : 4;
+  constexpr int NPQ = 4 / EPQ;
+  static_for<FM * (FN / EPN) * NPQ>([&](auto pass) {
+    constexpr int mi = decltype(pass)::value / (FN / EPN * NPQ);
+    constexpr int n0 = decltype(pass)::value / NPQ % (FN / EPN) * EPN;
+    constexpr int q0 = decltype(pass)::value % NPQ * EPQ;
     const int ib = i_base + mi * 32 + 4 * hsel;  // + 8q + t
-    // phase 1: the inputs of this 32-row block
-    float ein[FN][16];
-    float win[EPI == EPI_FINAL_W ? FN : 1][16];
-    static_for<FN>([&](auto ni) {
-      const int j = j_base + ni * 32 + (lane & 31);
-      static_for<16>([&](auto r) {
-        const int i = ib + 8 * (r / 4) + (r % 4);
-        if constexpr (EPI == EPI_POLY) ein[ni][r] = to_f32(Ain[(long long)i * a.ldc + j]);
-        if constexpr (EPI == EPI_UPDATE || FINAL) ein[ni][r] = Xf[(long long)i * a.ldx + j];
+    // phase 1: the inputs of this pass
+    float ein[EPN][4 * EPQ];
+    float win[EPI == EPI_FINAL_W ? EPN : 1][4 * EPQ];
+    static_for<EPN>([&](auto nn) {
+      const int j = j_base + (n0 + nn) * 32 + (lane & 31);
+      static_for<4 * EPQ>([&](auto e) {
+        const int i = ib + 8 * (q0 + e / 4) + (e % 4);
+        if constexpr (EPI == EPI_POLY) ein[nn][e] = to_f32(Ain[(long long)i * a.ldc + j]);
+        if constexpr (EPI == EPI_UPDATE || FINAL) {
+          const long long o = (long long)i * a.ldx + j;
+          if constexpr (HILO) ein[nn][e] = to_f32(Xh[o]) + to_f32(Xl[o]);
+          else ein[nn][e] = Xf[o];
+        }
         if constexpr (EPI == EPI_FINAL_W) {
           // outside the matrix (zero padding) read element 0 and discard it
           const bool inb = i < a.m && j < a.n;
           const long long oo = tall ? (long long)j * a.m + i : (long long)i * a.n + j;
-          win[ni][r] = W[inb ? oo : 0];
+          win[nn][e] = W[inb ? oo : 0];
         }
       });
     });
     // phase 2: values, direct stores, transposed staging
-    static_for<FN>([&](auto ni) {
+    static_for<EPN>([&](auto nn) {
+      constexpr int ni = n0 + decltype(nn)::value;
       const int j = j_base + ni * 32 + (lane & 31);
-      static_for<4>([&](auto q) {
+      static_for<EPQ>([&](auto qq) {
+        constexpr int q = q0 + decltype(qq)::value;
         float v[4];
         static_for<4>([&](auto t) {
-          constexpr int r = 4 * q + t;
+          constexpr int r = 4 * q + t;           // accumulator register
+          constexpr int e = 4 * decltype(qq)::value + t;  // input of this pass
           const int i = ib + 8 * q + t;
           const float accv = acc[mi][ni][r];
           if constexpr (EPI == EPI_GRAM) {
             v[t] = accv * alpha;
             C[(long long)i * a.ldc + j] = from_f32<T>(v[t]);
           } else if constexpr (EPI == EPI_POLY) {
-            v[t] = a.b * ein[ni][r] + a.c * accv;
+            v[t] = a.b * ein[nn][e] + a.c * accv;
             C[(long long)i * a.ldc + j] = from_f32<T>(v[t]);
           } else if constexpr (EPI == EPI_UPDATE) {
-            v[t] = scl * (a.a * ein[ni][r] + accv);
+            v[t] = scl * (a.a * ein[nn][e] + accv);
             const long long o = (long long)i * a.ldx + j;
-            Xf[o] = v[t];
-            if (Xb) Xb[o] = from_f32<bf16_t>(v[t]);
+            if constexpr (HILO) {
+              // lo is updated in place: only this block reads X[i][j]'s lo
+              bf16_t hi, lo;
+              split_bf16(v[t], hi, lo);
+              Xh_next[o] = hi;
+              Xl[o] = lo;
+            } else {
+              Xf[o] = v[t];
+            }
           } else {  // FINAL_W, FINAL_OUT
-            const float x = scl * (a.a * ein[ni][r] + accv);
+            const float x = scl * (a.a * ein[nn][e] + accv);
             if (i < a.m && j < a.n) {
               const long long oo = tall ? (long long)j * a.m + i : (long long)i * a.n + j;
               if constexpr (EPI == EPI_FINAL_W) {
-                W[oo] = fmaf(wscale, x, win[ni][r]);
+                W[oo] = fmaf(wscale, x, win[nn][e]);
               } else if (a.out_bf16) {
                 static_cast<bf16_t*>(a.out)[(long long)mat * a.s_out + oo] = from_f32<bf16_t>(x);
               } else {
@@ -613,7 +716,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
             }
           }
         });
-        if constexpr (!FINAL) {
+        if constexpr (STAGED_T) {
           if (stage_t) {
             const int il = wm * WTM + mi * 32 + 8 * q + 4 * hsel, jl = jl0 + ni * 32;
             if constexpr (sizeof(T) == 2) {
@@ -633,7 +736,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
       });
     });
   });
-  if constexpr (!FINAL) {
+  if constexpr (STAGED_T) {
     if (stage_t) {
       __syncthreads();
       T* __restrict__ dst;
@@ -645,10 +748,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
         dst = C;
         ld = a.ldc;
       }
-      constexpr int CPR = BM / EPC;  // 16-byte chunks per transposed row
+      constexpr int CPT = BM / EPC;  // 16-byte chunks per transposed row
 #pragma unroll 4
-      for (int c = tid; c < BN * CPR; c += NT) {
-        const int jl = c / CPR, il = (c % CPR) * EPC;
+      for (int c = tid; c < BN * CPT; c += NT) {
+        const int jl = c / CPT, il = (c % CPT) * EPC;
         *reinterpret_cast<u32x4_t*>(dst + (long long)(tj * BN + jl) * ld + ti * BM + il) =
             *reinterpret_cast<const u32x4_t*>(Ts + jl * TLD + il);
       }
@@ -661,7 +764,8 @@ hipError_t launch_prep(int grad_bf16, int compute_bf16, int momentum, const Prep
                        const PrepTable& t, int batch, hipStream_t s) {
   const dim3 grid(a.nblk, batch), block(256);
   const PrepLaunch launch{a, t};
-#define MUON_PREP(GT, CT, MOM) hipLaunchKernelGGL((prep_kernel<GT, CT, MOM>), grid, block, 0, s, launch)
+#define MUON_PREP(GT, CT, MOM) \
+  hipLaunchKernelGGL((prep_kernel<GT, CT, MOM>), grid, block, 0, s, launch)
   if (grad_bf16) {
     if (compute_bf16) {
       if (momentum) MUON_PREP(bf16_t, bf16_t, true); else MUON_PREP(bf16_t, bf16_t, false);
@@ -692,12 +796,11 @@ int gemm_tile(int compute_bf16, int tile_pref) {
 
 // bf16 256x256 tiles on 8 waves (2x4, 128x64 each).  Main loop, chosen by
 // MUON_WAVE_CFG (a tuning knob; by default 5 for GRAM / POLY, 4 otherwise):
-//   0  register-staged loads, 128-byte rows, two LDS stages
-//   1  direct-to-LDS loads, 64-byte rows, 3 stages
-//   3  as 1 with the MFMA / LDS-read order pinned
-//   4  direct-to-LDS loads, 128-byte rows, 2 stages, order pinned
+//   0  register-staged loads, two LDS stages
+//   4  direct-to-LDS loads, two stages, order pinned
 //   5  as 4 with the stage hand-over one k-substep before the tile's end
-// 128x128 tiles use 4 waves (64x64 each) and register-staged loads.
+// 128x128 tiles use 4 waves (64x64 each) and register-staged loads.  The
+// bf16 UPDATE / FINAL read X's hi plane as a row-major second operand.
 static int wave_cfg(int epi) {
   static const int v = [] {
     const char* e = std::getenv("MUON_WAVE_CFG");
@@ -711,33 +814,28 @@ template <typename T, int E>
 static void launch_gemm_t(int tile, const GemmArgs& a, const WeightTable& t, dim3 grid,
                           hipStream_t s) {
   const GemmLaunch launch{a, t};
+  constexpr bool QR =
+      sizeof(T) == 2 && (E == EPI_UPDATE || E == EPI_FINAL_W || E == EPI_FINAL_OUT);
   if constexpr (sizeof(T) == 2) {
     if (tile == 256) {
       switch (wave_cfg(E)) {
         case 0:
-          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 0, 128>), grid, dim3(512), 0, s,
-                             launch);
-          return;
-        case 1:
-          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 3, 64>), grid, dim3(512), 0, s,
-                             launch);
-          return;
-        case 3:
-          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 3, 64, true>), grid, dim3(512), 0,
-                             s, launch);
+          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 0, false, false, QR>), grid,
+                             dim3(512), 0, s, launch);
           return;
         case 5:
-          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 2, 128, true, true>), grid,
+          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 2, true, true, QR>), grid,
                              dim3(512), 0, s, launch);
           return;
         default:
-          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 2, 128, true>), grid, dim3(512), 0,
-                             s, launch);
+          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 2, true, false, QR>), grid,
+                             dim3(512), 0, s, launch);
           return;
       }
     }
   }
-  hipLaunchKernelGGL((gemm_kernel<T, E, 128, 128, 2, 2, 0, 128>), grid, dim3(256), 0, s, launch);
+  hipLaunchKernelGGL((gemm_kernel<T, E, 128, 128, 2, 2, 0, false, false, QR>), grid, dim3(256),
+                     0, s, launch);
 }
 
 hipError_t launch_gemm(int compute_bf16, int epi, int tile, const GemmArgs& a_in,
