@@ -248,19 +248,36 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
     g.group_m = group_m();
     g.out = c.out; g.s_out = c.s_out; g.out_bf16 = c.out_bf16;
     g.neg_lr = c.neg_lr;
+    // tall matrices: runs of 4 elements of a stored row (length m) are
+    // aligned when m and the output's matrix stride are multiples of 4
+    g.vec_tall = L.m % 4 == 0 && (c.final_mode != FINAL_OUT || c.s_out % 4 == 0);
     // reads B and the operand X; the epilogue reads X (bf16: hi + lo, fp32:
     // X) and writes the next X (bf16: hi + lo, fp32: X + X^T), or, on the
     // last step, reads and writes the weights or writes the output
-    const double upd_bytes =
-        pmm * es + pmn * es + pmn * 4.0 +
-        (last ? (c.final_mode == FINAL_WEIGHTS ? elems * 8.0 : elems * (c.out_bf16 ? 2.0 : 4.0))
-              : pmn * (cbf16 ? 4.0 : 8.0));
-    err = timed(last ? MUON_K_FINAL : MUON_K_UPDATE, L.m, L.n, c.cnt, k, cnt * 2.0 * m * m * n,
-                upd_bytes, s,
-                [&] { return launch_gemm(cbf16, !last ? EPI_UPDATE
-                                             : c.final_mode == FINAL_WEIGHTS ? EPI_FINAL_W
-                                                                             : EPI_FINAL_OUT,
-                                     tile_upd, g, c.wt, c.cnt, s); });
+    if (!last) {
+      const double upd_bytes = pmm * es + pmn * es + pmn * 4.0 + pmn * (cbf16 ? 4.0 : 8.0);
+      err = timed(MUON_K_UPDATE, L.m, L.n, c.cnt, k, cnt * 2.0 * m * m * n, upd_bytes, s,
+                  [&] { return launch_gemm(cbf16, EPI_UPDATE, tile_upd, g, c.wt, c.cnt, s); });
+    } else {
+      // The chunk holds its wide matrices first, then the tall ones, which
+      // store the result transposed; each part has its own launch.
+      const int ntall = __builtin_popcountll(c.tall_mask);
+      const int nwide = c.cnt - ntall;
+      for (int part = 0; part < 2 && err == hipSuccess; ++part) {
+        const int b = part == 0 ? nwide : ntall;
+        if (b == 0) continue;
+        GemmArgs gf = g;
+        gf.mat0 = part == 0 ? 0 : nwide;
+        const int epi = c.final_mode == FINAL_WEIGHTS ? (part ? EPI_FINAL_W_T : EPI_FINAL_W)
+                                                      : (part ? EPI_FINAL_OUT_T : EPI_FINAL_OUT);
+        const double bm = b, pmn_b = bm * (double)MN, el_b = m * n * bm;
+        const double fin_bytes = bm * (double)MM * es + pmn_b * es + pmn_b * 4.0 +
+                                 (c.final_mode == FINAL_WEIGHTS ? el_b * 8.0
+                                                                : el_b * (c.out_bf16 ? 2.0 : 4.0));
+        err = timed(MUON_K_FINAL, L.m, L.n, b, k, bm * 2.0 * m * m * n, fin_bytes, s,
+                    [&] { return launch_gemm(cbf16, epi, tile_upd, gf, c.wt, b, s); });
+      }
+    }
     if (err != hipSuccess) return MUON_ERR_HIP;
   }
   return MUON_OK;
@@ -434,8 +451,17 @@ int muon_step(int n, const int* rows, const int* cols, void* const* params, int 
       // Tall and wide matrices of one oriented shape share the launch: the
       // kernels read each matrix's orientation from the mask.
       Chunk c{};
+      // wide matrices first, then the tall ones (the last step launches the
+      // two orientations separately, each over a contiguous range)
+      int order[kChunk];
+      int no = 0;
+      for (int pass = 0; pass < 2; ++pass)
+        for (int q = 0; q < cnt; ++q) {
+          const int i = g.idx[b0 + q];
+          if ((rows[i] > cols[i]) == (pass == 1)) order[no++] = i;
+        }
       for (int q = 0; q < cnt; ++q) {
-        const int i = g.idx[b0 + q];
+        const int i = order[q];
         c.pt.g[q] = grads[i];
         c.pt.buf[q] = momentum[i];
         c.wt.w[q] = static_cast<float*>(params[i]);

@@ -17,8 +17,12 @@ constexpr int kPrepTile = 64;
 // GEMM epilogues: GRAM A = inv^2 X X^T; POLY B = b A + c A A; UPDATE
 // X <- scl (a X + B X) written as the next X state; FINAL_W the same value
 // subtracted (times lr * scale) from the weights; FINAL_OUT the same value
-// written to the caller's output.
-enum Epi { EPI_GRAM = 0, EPI_POLY = 1, EPI_UPDATE = 2, EPI_FINAL_W = 3, EPI_FINAL_OUT = 4 };
+// written to the caller's output.  The _T variants are the FINALs of tall
+// matrices (stored transposed to the oriented X).
+enum Epi {
+  EPI_GRAM = 0, EPI_POLY = 1, EPI_UPDATE = 2, EPI_FINAL_W = 3, EPI_FINAL_OUT = 4,
+  EPI_FINAL_W_T = 5, EPI_FINAL_OUT_T = 6
+};
 enum Final { FINAL_NONE = 0, FINAL_OUT = 1, FINAL_WEIGHTS = 2 };
 
 // Inputs of the prep kernel: momentum (step) or plain input (orthogonalize),
@@ -58,6 +62,7 @@ struct GemmArgs {
   int ldp, ldq, K;
   int tiles_m, tiles_n;
   int tiles_per_mat;       // set by launch_gemm
+  int mat0;                // the launch covers matrices mat0 .. mat0 + batch - 1
   int group_m;             // full grids: tile rows per scheduling group
   int tri;                 // 1: lower-triangle tiles only (GRAM, POLY)
   const float* inv;        // first step: 1/(||u||_F+eps) per matrix, else null
@@ -74,6 +79,8 @@ struct GemmArgs {
   unsigned long long tall_mask;          // bit i: matrix i is stored tall
   int final_mode;
   void* out; long long s_out; int out_bf16;
+  int vec_tall;            // FINAL of tall matrices: 4 consecutive i of a
+                           // weight / output row are 16- (8-) byte aligned
   float neg_lr;
 };
 

@@ -212,8 +212,9 @@ __device__ __forceinline__ int xcd_remap(int w, int total) {
 __device__ __forceinline__ void decode_tile(const GemmArgs& a, int& mat, int& ti, int& tj) {
   const int total = a.tiles_per_mat * (int)gridDim.y;
   const int L = xcd_remap((int)blockIdx.x + (int)blockIdx.y * (int)gridDim.x, total);
-  mat = L / a.tiles_per_mat;
-  const int t = L - mat * a.tiles_per_mat;
+  const int lm = L / a.tiles_per_mat;
+  const int t = L - lm * a.tiles_per_mat;
+  mat = a.mat0 + lm;
   if (a.tri) {
     tri_decode(t, ti, tj);
   } else {
@@ -354,7 +355,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
   constexpr size_t MAIN_BYTES = 2 * (size_t)STAGE * 16;
   constexpr size_t EPI_BYTES = (size_t)BN * TLD * sizeof(T);
   constexpr size_t LDS_BYTES = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
-  constexpr bool FINAL = EPI == EPI_FINAL_W || EPI == EPI_FINAL_OUT;
+  constexpr bool FIN_W = EPI == EPI_FINAL_W || EPI == EPI_FINAL_W_T;
+  constexpr bool FIN_OUT = EPI == EPI_FINAL_OUT || EPI == EPI_FINAL_OUT_T;
+  constexpr bool FINAL = FIN_W || FIN_OUT;
+  constexpr bool TALLF = EPI == EPI_FINAL_W_T || EPI == EPI_FINAL_OUT_T;  // FINAL, tall matrices
   constexpr bool HILO = sizeof(T) == 2;  // bf16 path: X state as hi + lo planes
   constexpr bool STAGED_T = EPI == EPI_GRAM || EPI == EPI_POLY || (EPI == EPI_UPDATE && !HILO);
   static_assert(FM * 32 * WGM == BM && FN * 32 * WGN == BN, "wave tiles must be 32-aligned");
@@ -606,7 +610,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
     alpha = v * v;
     scl = v;
   }
-  const bool tall = (a.tall_mask >> mat) & 1ull;
+  constexpr bool tall = TALLF;
   // Transposed output of this block: the mirrored tile (GRAM, POLY off the
   // diagonal) or, on the fp32 path, the next step's X^T (UPDATE).
   bool stage_t = false;
@@ -630,7 +634,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
     } else {
       Xf = a.Xf + (long long)mat * a.sX;
     }
-    if constexpr (EPI == EPI_FINAL_W) {
+    if constexpr (FIN_W) {
       W = kernarg<GemmLaunch>().wt.w[mat];
       wscale = a.neg_lr * kernarg<GemmLaunch>().wt.scale[mat];
     }
@@ -640,11 +644,127 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
   }
   const int jl0 = wn * WTN + (lane & 31);
 
+  // FINAL of a tall matrix: the weight (output) is stored transposed to the
+  // oriented X, so each lane's 4 consecutive rows i of one column j are
+  // contiguous in memory but neighbouring lanes are a row of W apart.  Each
+  // 32-row block of every wave goes through LDS instead, as [j][i] rows of
+  // 16-byte chunks (chunk c of row j at slot c ^ (j % SCH)), and the block
+  // then updates whole 16-byte runs of W's rows, coalesced.
+  if constexpr (TALLF) {
+    {
+      constexpr int SR = 32 * WGM;  // staged i per j row
+      constexpr int SCH = SR / 4;   // 16-byte chunks per staged row
+      constexpr int NCH = BN * SCH;
+      constexpr int PERT = NCH / NT;
+      static_assert(PERT * NT == NCH, "staged chunks must split over the threads");
+      static_assert((size_t)NCH * 16 <= (QROW ? (size_t)STAGE * 16 : LDS_BYTES), "staging fits");
+      float* __restrict__ Tf = QROW ? reinterpret_cast<float*>(S0) : reinterpret_cast<float*>(smem);
+      static_for<FM>([&](auto mi) {
+        const int ib = i_base + mi * 32 + 4 * hsel;  // + 8q + t
+        static_for<FN>([&](auto ni) {
+          const int j = j_base + ni * 32 + (lane & 31);
+          float ein[16];
+          static_for<16>([&](auto r) {
+            const long long o = (long long)(ib + 8 * (r / 4) + (r % 4)) * a.ldx + j;
+            if constexpr (HILO) ein[r] = to_f32(Xh[o]) + to_f32(Xl[o]);
+            else ein[r] = Xf[o];
+          });
+          const int jl = jl0 + ni * 32;
+          static_for<4>([&](auto q) {
+            f32x4_t f;
+            static_for<4>([&](auto t) {
+              constexpr int r = 4 * q + t;
+              f[(int)t] = scl * (a.a * ein[r] + acc[mi][ni][r]);
+            });
+            const int c = (wm * 32 + 8 * q + 4 * hsel) >> 2;
+            *reinterpret_cast<f32x4_t*>(Tf + jl * SR + ((c ^ (jl % SCH)) << 2)) = f;
+          });
+        });
+        __syncthreads();
+        constexpr int HALF = PERT >= 4 ? 4 : PERT;  // runs per write-back round
+        static_assert(PERT % HALF == 0, "write-back rounds");
+#pragma unroll
+        for (int s0 = 0; s0 < PERT; s0 += HALF) {
+          f32x4_t xv[HALF];
+          long long off[HALF];
+          int nval[HALF];  // valid elements of the run (0 .. 4)
+#pragma unroll
+          for (int s = 0; s < HALF; ++s) {
+            const int cc = tid + NT * (s0 + s), jl = cc / SCH, c = cc % SCH;
+            xv[s] = *reinterpret_cast<const f32x4_t*>(Tf + jl * SR + ((c ^ (jl % SCH)) << 2));
+            const int il = 4 * c;
+            const int i = ti * BM + (il / 32) * WTM + mi * 32 + il % 32;
+            const int j = tj * BN + jl;
+            const int rem = a.m - i;
+            nval[s] = j < a.n ? (rem < 0 ? 0 : rem > 4 ? 4 : rem) : 0;
+            off[s] = (long long)j * a.m + i;
+          }
+          if constexpr (FIN_W) {
+            f32x4_t wv[HALF];
+#pragma unroll
+            for (int s = 0; s < HALF; ++s) {
+              if (a.vec_tall && nval[s] == 4) {
+                wv[s] = *reinterpret_cast<const f32x4_t*>(W + off[s]);
+              } else {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) wv[s][t] = t < nval[s] ? W[off[s] + t] : 0.f;
+              }
+            }
+#pragma unroll
+            for (int s = 0; s < HALF; ++s) {
+              f32x4_t w;
+#pragma unroll
+              for (int t = 0; t < 4; ++t) w[t] = fmaf(wscale, xv[s][t], wv[s][t]);
+              if (a.vec_tall && nval[s] == 4) {
+                *reinterpret_cast<f32x4_t*>(W + off[s]) = w;
+              } else {
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                  if (t < nval[s]) W[off[s] + t] = w[t];
+              }
+            }
+          } else {
+#pragma unroll
+            for (int s = 0; s < HALF; ++s) {
+              const long long o = (long long)mat * a.s_out + off[s];
+              if (a.out_bf16) {
+                bf16_t* ob = static_cast<bf16_t*>(a.out) + o;
+                if (a.vec_tall && nval[s] == 4) {
+                  uint2 pk;
+                  pk.x = (unsigned)__builtin_bit_cast(unsigned short, from_f32<bf16_t>(xv[s][0])) |
+                         ((unsigned)__builtin_bit_cast(unsigned short, from_f32<bf16_t>(xv[s][1])) << 16);
+                  pk.y = (unsigned)__builtin_bit_cast(unsigned short, from_f32<bf16_t>(xv[s][2])) |
+                         ((unsigned)__builtin_bit_cast(unsigned short, from_f32<bf16_t>(xv[s][3])) << 16);
+                  *reinterpret_cast<uint2*>(ob) = pk;
+                } else {
+#pragma unroll
+                  for (int t = 0; t < 4; ++t)
+                    if (t < nval[s]) ob[t] = from_f32<bf16_t>(xv[s][t]);
+                }
+              } else {
+                float* of = static_cast<float*>(a.out) + o;
+                if (a.vec_tall && nval[s] == 4) {
+                  *reinterpret_cast<f32x4_t*>(of) = xv[s];
+                } else {
+#pragma unroll
+                  for (int t = 0; t < 4; ++t)
+                    if (t < nval[s]) of[t] = xv[s][t];
+                }
+              }
+            }
+          }
+        }
+        __syncthreads();  // the staging tile is rewritten by the next block
+      });
+      return;
+    }
+  }
+
   // Epilogue passes: EPN accumulator column blocks and EPQ of the 4 row
   // quads of one 32-row block at a time (FINAL_W has a third input, so its
   // passes are smaller to keep the loads in flight within the registers).
-  constexpr int EPN = EPI == EPI_FINAL_W ? 1 : FN;
-  constexpr int EPQ = EPI == EPI_FINAL_W ? 2 : 4;
+  constexpr int EPN = FIN_W ? 1 : FN;
+  constexpr int EPQ = FIN_W ? 2 : 4;
   constexpr int NPQ = 4 / EPQ;
   static_for<FM * (FN / EPN) * NPQ>([&](auto pass) {
     constexpr int mi = decltype(pass)::value / (FN / EPN * NPQ);
@@ -653,7 +773,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
     const int ib = i_base + mi * 32 + 4 * hsel;  // + 8q + t
     // phase 1: the inputs of this pass
     float ein[EPN][4 * EPQ];
-    float win[EPI == EPI_FINAL_W ? EPN : 1][4 * EPQ];
+    float win[FIN_W ? EPN : 1][4 * EPQ];
     static_for<EPN>([&](auto nn) {
       const int j = j_base + (n0 + nn) * 32 + (lane & 31);
       static_for<4 * EPQ>([&](auto e) {
@@ -664,7 +784,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
           if constexpr (HILO) ein[nn][e] = to_f32(Xh[o]) + to_f32(Xl[o]);
           else ein[nn][e] = Xf[o];
         }
-        if constexpr (EPI == EPI_FINAL_W) {
+        if constexpr (FIN_W) {
           // outside the matrix (zero padding) read element 0 and discard it
           const bool inb = i < a.m && j < a.n;
           const long long oo = tall ? (long long)j * a.m + i : (long long)i * a.n + j;
@@ -706,7 +826,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
             const float x = scl * (a.a * ein[nn][e] + accv);
             if (i < a.m && j < a.n) {
               const long long oo = tall ? (long long)j * a.m + i : (long long)i * a.n + j;
-              if constexpr (EPI == EPI_FINAL_W) {
+              if constexpr (FIN_W) {
                 W[oo] = fmaf(wscale, x, win[nn][e]);
               } else if (a.out_bf16) {
                 static_cast<bf16_t*>(a.out)[(long long)mat * a.s_out + oo] = from_f32<bf16_t>(x);
@@ -795,10 +915,11 @@ int gemm_tile(int compute_bf16, int tile_pref) {
 }
 
 // bf16 256x256 tiles on 8 waves (2x4, 128x64 each).  Main loop, chosen by
-// MUON_WAVE_CFG (a tuning knob; by default 5 for GRAM / POLY, 4 otherwise):
+// MUON_WAVE_CFG (a tuning knob; 5 by default):
 //   0  register-staged loads, two LDS stages
 //   4  direct-to-LDS loads, two stages, order pinned
 //   5  as 4 with the stage hand-over one k-substep before the tile's end
+//   6, 7  as 4, 5 on 4 waves (2x2, 128x128 each, accumulators in AGPRs)
 // 128x128 tiles use 4 waves (64x64 each) and register-staged loads.  The
 // bf16 UPDATE / FINAL read X's hi plane as a row-major second operand.
 static int wave_cfg(int epi) {
@@ -806,8 +927,8 @@ static int wave_cfg(int epi) {
     const char* e = std::getenv("MUON_WAVE_CFG");
     return e ? std::atoi(e) : -1;
   }();
-  if (v >= 0) return v;
-  return epi == EPI_GRAM || epi == EPI_POLY ? 5 : 4;
+  (void)epi;
+  return v >= 0 ? v : 5;
 }
 
 template <typename T, int E>
@@ -815,7 +936,7 @@ static void launch_gemm_t(int tile, const GemmArgs& a, const WeightTable& t, dim
                           hipStream_t s) {
   const GemmLaunch launch{a, t};
   constexpr bool QR =
-      sizeof(T) == 2 && (E == EPI_UPDATE || E == EPI_FINAL_W || E == EPI_FINAL_OUT);
+      sizeof(T) == 2 && E != EPI_GRAM && E != EPI_POLY;
   if constexpr (sizeof(T) == 2) {
     if (tile == 256) {
       switch (wave_cfg(E)) {
@@ -826,6 +947,14 @@ static void launch_gemm_t(int tile, const GemmArgs& a, const WeightTable& t, dim
         case 5:
           hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 2, true, true, QR>), grid,
                              dim3(512), 0, s, launch);
+          return;
+        case 6:
+          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 2, 2, true, false, QR>), grid,
+                             dim3(256), 0, s, launch);
+          return;
+        case 7:
+          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 2, 2, true, true, QR>), grid,
+                             dim3(256), 0, s, launch);
           return;
         default:
           hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 2, true, false, QR>), grid,
@@ -849,14 +978,18 @@ hipError_t launch_gemm(int compute_bf16, int epi, int tile, const GemmArgs& a_in
     else if (epi == EPI_POLY) launch_gemm_t<bf16_t, EPI_POLY>(tile, a, t, grid, s);
     else if (epi == EPI_UPDATE) launch_gemm_t<bf16_t, EPI_UPDATE>(tile, a, t, grid, s);
     else if (epi == EPI_FINAL_W) launch_gemm_t<bf16_t, EPI_FINAL_W>(tile, a, t, grid, s);
-    else launch_gemm_t<bf16_t, EPI_FINAL_OUT>(tile, a, t, grid, s);
+    else if (epi == EPI_FINAL_OUT) launch_gemm_t<bf16_t, EPI_FINAL_OUT>(tile, a, t, grid, s);
+    else if (epi == EPI_FINAL_W_T) launch_gemm_t<bf16_t, EPI_FINAL_W_T>(tile, a, t, grid, s);
+    else launch_gemm_t<bf16_t, EPI_FINAL_OUT_T>(tile, a, t, grid, s);
   } else {
     // fp32 path: 128 x 128 tiles (the transposed epilogue tile fits in LDS)
     if (epi == EPI_GRAM) launch_gemm_t<float, EPI_GRAM>(128, a, t, grid, s);
     else if (epi == EPI_POLY) launch_gemm_t<float, EPI_POLY>(128, a, t, grid, s);
     else if (epi == EPI_UPDATE) launch_gemm_t<float, EPI_UPDATE>(128, a, t, grid, s);
     else if (epi == EPI_FINAL_W) launch_gemm_t<float, EPI_FINAL_W>(128, a, t, grid, s);
-    else launch_gemm_t<float, EPI_FINAL_OUT>(128, a, t, grid, s);
+    else if (epi == EPI_FINAL_OUT) launch_gemm_t<float, EPI_FINAL_OUT>(128, a, t, grid, s);
+    else if (epi == EPI_FINAL_W_T) launch_gemm_t<float, EPI_FINAL_W_T>(128, a, t, grid, s);
+    else launch_gemm_t<float, EPI_FINAL_OUT_T>(128, a, t, grid, s);
   }
   return hipGetLastError();
 }

@@ -178,3 +178,39 @@ def test_stress_logspec_reduced_size():
         cf = gram_closed_form(x0, [wl.CUBIC] * 30)
         cf = cf if g.shape[0] <= g.shape[1] else cf.T
         assert oracle.relative_frobenius_error(ref, cf) <= 1e-8
+
+
+@pytest.mark.parametrize("compute", ["bf16", "fp32"])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("pad", [0, 1, 4])
+def test_tall_batch_stride_through_c_abi(compute, out_dtype, pad):
+    # Tall matrices store the result transposed to the oriented X; with
+    # m % 4 == 0 the result rows are written in aligned runs of 4 unless the
+    # batch stride breaks the alignment (pad 1), which must give the same values.
+    announce("tall batch stride", compute, out_dtype, pad)
+    from muon_newton_schulz_step_amd import _lib
+    batch, rows, cols = 3, 300, 44
+    stride = rows * cols + pad
+    x = wl.gaussian_batch(batch, rows, cols, seed=11, device=DEV)
+    xin = torch.zeros(batch * stride, dtype=torch.float32, device=DEV)
+    out = torch.full((batch * stride,), 7.0, dtype=out_dtype, device=DEV)
+    for b in range(batch):
+        xin[b * stride:b * stride + rows * cols] = x[b].reshape(-1)
+    lib = mn.lib()
+    c = 0 if compute == "bf16" else 1
+    need = lib.muon_orthogonalize_workspace_bytes(batch, rows, cols, c)
+    ws = torch.empty(need + 256, dtype=torch.uint8, device=DEV)
+    wp = (ws.data_ptr() + 255) // 256 * 256
+    st = lib.muon_orthogonalize(
+        xin.data_ptr(), _lib.MUON_FP32, out.data_ptr(),
+        _lib.MUON_BF16 if out_dtype == torch.bfloat16 else _lib.MUON_FP32,
+        batch, rows, cols, stride, _lib.coeff_array(Q5), 5, 1e-7, c, wp, need, None)
+    assert st == _lib.MUON_OK
+    torch.cuda.synchronize()
+    extra = 4e-3 if out_dtype == torch.bfloat16 else 0.0
+    for b in range(batch):
+        o = out[b * stride:b * stride + rows * cols].reshape(rows, cols)
+        ref = oracle.orthogonalize(to64(x[b]), Q5)
+        assert oracle.relative_frobenius_error(to64(o), ref) <= tol(compute) + extra, b
+        if pad:  # the gap between matrices is not written
+            assert torch.all(out[b * stride + rows * cols:(b + 1) * stride] == 7.0)
