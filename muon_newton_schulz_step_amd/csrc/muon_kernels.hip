@@ -298,6 +298,24 @@ __device__ __forceinline__ void load_lds16(const void* src, void* lds_wave_base)
 #endif
 }
 
+// The same 16-byte direct-to-LDS load through a buffer resource (MUBUF).
+// A global (FLAT-encoded) load that writes LDS counts as pending on both the
+// vector-memory and the LDS counters, which forces every LDS wait behind it
+// to drain all LDS reads (lgkmcnt(0)); the buffer form counts on vmcnt only.
+// Buffer resource word 3 on gfx9-family chips: 32-bit data format, no
+// swizzle; stride 0 (raw), range 0xffffffff (no range clamping).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)0xffffffff,
+                                           0x00020000);
+}
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, unsigned voffset,
+                                                  void* lds_wave_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rsrc, (__attribute__((address_space(3))) void*)lds_wave_base, 16, (int)voffset, 0, 0, 0);
+#endif
+}
+
 // Transposing LDS read of 4 x 16 bits (ds_read_b64_tr_b16), 8-byte aligned
 // addresses.  In each group of 16 lanes, lane i receives element i % 4 of
 // the 8-byte rows addressed by lanes i/4, i/4 + 4, i/4 + 8 and i/4 + 12, in
@@ -337,7 +355,7 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const void* p) {
 // mirrored triangle of A and B, the fp32 path's X^T) are staged in LDS as
 // [j][i] rows and stored as coalesced 16-byte chunks.
 template <typename T, int EPI, int BM, int BN, int WGM, int WGN, int S, bool SCHED, bool EARLY,
-          bool QROW>
+          bool QROW, bool SPREAD = false, bool BUFLD = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch) {
   const GemmArgs& a = launch.a;
   constexpr int NT = 64 * WGM * WGN, NW = WGM * WGN;
@@ -471,9 +489,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
   // MFMA followed by one read of the next substep's operands.
   constexpr int NREAD = FM + (QROW ? 2 * FN : FN);
   constexpr int NPAIR = NREAD < FM * FN ? NREAD : FM * FN;
-  auto schedule_substeps = [&](int n) {
+  // (vmem: loads issued first in each substep, a std::integral_constant)
+  auto schedule_substeps = [&](int n, auto vmem) {
     if constexpr (SCHED) {
       for (int kk = 0; kk < n; ++kk) {
+        if constexpr (decltype(vmem)::value > 0)
+          __builtin_amdgcn_sched_group_barrier(0x020, decltype(vmem)::value, 0);
 #pragma unroll
         for (int x = 0; x < NPAIR; ++x) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
@@ -495,7 +516,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
     }
     if constexpr (SCHED) {
       __builtin_amdgcn_sched_group_barrier(0x100, NREAD, 0);
-      schedule_substeps(KK - 1);
+      schedule_substeps(KK - 1, std::integral_constant<int, 0>{});
       __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
     }
   };
@@ -547,11 +568,27 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
     const T* src[DPW];
 #pragma unroll
     for (int d = 0; d < DPW; ++d) src[d] = chunk_src((wave * DPW + d) * 64 + lane);
-    auto issue = [&](int kt, u32x4_t* St) {
-      const long long off = kt * kstep;
+    // BUFLD: the wave's operand panel as a buffer resource, rebased per k-tile,
+    // and 32-bit lane offsets into it (the host checks that they fit)
+    const T* wbase = wave_s * DPW * 64 < P_CHUNKS ? Pm : Qm;
+    unsigned voff[BUFLD ? DPW : 1];
+    if constexpr (BUFLD) {
 #pragma unroll
-      for (int d = 0; d < DPW; ++d) load_lds16(src[d] + off, St + (wave_s * DPW + d) * 64);
+      for (int d = 0; d < DPW; ++d) voff[d] = (unsigned)((src[d] - wbase) * (long long)sizeof(T));
+    }
+    // loads d0 .. d1 - 1 of k-tile kt into stage St
+    auto issue_range = [&](int kt, u32x4_t* St, int d0, int d1) {
+      const long long off = kt * kstep;
+      if constexpr (BUFLD) {
+        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(wbase + off);
+#pragma unroll
+        for (int d = d0; d < d1; ++d) buffer_load_lds16(rs, voff[d], St + (wave_s * DPW + d) * 64);
+      } else {
+#pragma unroll
+        for (int d = d0; d < d1; ++d) load_lds16(src[d] + off, St + (wave_s * DPW + d) * 64);
+      }
     };
+    auto issue = [&](int kt, u32x4_t* St) { issue_range(kt, St, 0, DPW); };
     if constexpr (!EARLY) {
       auto ktile = [&](int kt, const u32x4_t* cur, u32x4_t* nxt) {
         wait_vmcnt<0>();     // this wave's part of k-tile kt has landed
@@ -571,27 +608,41 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
       // next k-tile's first operands are read while the last substep's MFMAs
       // run.  No branch in the body: the final two k-tiles reload the last
       // k-tile into a stage nobody reads any more (drained below).
-      auto ktile = [&](int kt, u32x4_t* cur, const u32x4_t* nxt) {
+      // SPREAD: a k-tile's loads go out in LG groups, the first right after
+      // the barrier that frees its stage, the others one per k-substep of
+      // the following k-tile, so that the waves never queue all their loads
+      // at the address unit at once (a wave waiting to issue a load cannot
+      // issue its MFMAs either).
+      constexpr int LG = SPREAD ? KK : 1;
+      constexpr int GPW = DPW / LG;  // loads per group
+      static_assert(GPW * LG == DPW, "load groups");
+      auto issue_group = [&](int kt, u32x4_t* St, int g) {
+        issue_range(kt, St, g * GPW, (g + 1) * GPW);
+      };
+      auto ktile = [&](int kt, u32x4_t* cur, u32x4_t* nxt) {
+        // the k-tile whose first load group went into nxt at the last barrier
+        const int kl = kt + 1 < nk ? kt + 1 : nk - 1;
 #pragma unroll
         for (int kk = 0; kk + 1 < KK; ++kk) {
+          if (kk + 1 < LG) issue_group(kl, nxt, kk + 1);
           fload(cur, kk + 1, (kk + 1) & 1);
           mfmas(kk & 1);
         }
-        schedule_substeps(KK - 1);
+        schedule_substeps(KK - 1, std::integral_constant<int, (LG > 1 ? GPW : 0)>{});
         wait_vmcnt<0>();     // this wave's part of k-tile kt+1 has landed
         barrier_no_fence();  // everyone's has; everyone is done reading cur
-        issue(kt + 2 < nk ? kt + 2 : nk - 1, cur);
+        issue_group(kt + 2 < nk ? kt + 2 : nk - 1, cur, 0);
         fload(nxt, 0, 0);
         mfmas((KK - 1) & 1);
         if constexpr (SCHED) {
-          __builtin_amdgcn_sched_group_barrier(0x020, DPW, 0);  // the loads
-          schedule_substeps(1);
+          __builtin_amdgcn_sched_group_barrier(0x020, GPW, 0);  // the loads
+          schedule_substeps(1, std::integral_constant<int, 0>{});
         }
       };
       issue(0, S0);
       wait_vmcnt<0>();
       barrier_no_fence();
-      issue(nk > 1 ? 1 : 0, S1);
+      issue_group(nk > 1 ? 1 : 0, S1, 0);
       fload(S0, 0, 0);
       for (int kt = 0; kt < nk; kt += 2) {
         ktile(kt, S0, S1);
@@ -915,11 +966,14 @@ int gemm_tile(int compute_bf16, int tile_pref) {
 }
 
 // bf16 256x256 tiles on 8 waves (2x4, 128x64 each).  Main loop, chosen by
-// MUON_WAVE_CFG (a tuning knob; 5 by default):
+// MUON_WAVE_CFG (a tuning knob; by default 9, and 5 for the FINALs, whose
+// epilogue-heavy tiles measured slower with buffer loads):
 //   0  register-staged loads, two LDS stages
 //   4  direct-to-LDS loads, two stages, order pinned
 //   5  as 4 with the stage hand-over one k-substep before the tile's end
 //   6, 7  as 4, 5 on 4 waves (2x2, 128x128 each, accumulators in AGPRs)
+//   8  as 5 with each k-tile's loads spread over the next k-tile's substeps
+//   9, 10  as 5, 8 with buffer (MUBUF) instead of global direct-to-LDS loads
 // 128x128 tiles use 4 waves (64x64 each) and register-staged loads.  The
 // bf16 UPDATE / FINAL read X's hi plane as a row-major second operand.
 static int wave_cfg(int epi) {
@@ -927,8 +981,10 @@ static int wave_cfg(int epi) {
     const char* e = std::getenv("MUON_WAVE_CFG");
     return e ? std::atoi(e) : -1;
   }();
-  (void)epi;
-  return v >= 0 ? v : 5;
+  if (v >= 0) return v;
+  const bool final = epi == EPI_FINAL_W || epi == EPI_FINAL_OUT || epi == EPI_FINAL_W_T ||
+                     epi == EPI_FINAL_OUT_T;
+  return final ? 5 : 9;
 }
 
 template <typename T, int E>
@@ -939,7 +995,13 @@ static void launch_gemm_t(int tile, const GemmArgs& a, const WeightTable& t, dim
       sizeof(T) == 2 && E != EPI_GRAM && E != EPI_POLY;
   if constexpr (sizeof(T) == 2) {
     if (tile == 256) {
-      switch (wave_cfg(E)) {
+      int cfg = wave_cfg(E);
+      // buffer loads address an operand panel with 32-bit lane offsets:
+      // up to 256 rows of the leading dimension
+      const long long ld = a.ldp > a.ldq ? a.ldp : a.ldq;
+      if ((cfg == 9 || cfg == 10) && 256LL * ld * (long long)sizeof(T) >= (1LL << 31))
+        cfg = cfg == 9 ? 5 : 8;
+      switch (cfg) {
         case 0:
           hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 0, false, false, QR>), grid,
                              dim3(512), 0, s, launch);
@@ -955,6 +1017,18 @@ static void launch_gemm_t(int tile, const GemmArgs& a, const WeightTable& t, dim
         case 7:
           hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 2, 2, true, true, QR>), grid,
                              dim3(256), 0, s, launch);
+          return;
+        case 8:
+          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 2, true, true, QR, true>), grid,
+                             dim3(512), 0, s, launch);
+          return;
+        case 9:
+          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 2, true, true, QR, false, true>),
+                             grid, dim3(512), 0, s, launch);
+          return;
+        case 10:
+          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 2, true, true, QR, true, true>),
+                             grid, dim3(512), 0, s, launch);
           return;
         default:
           hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 2, true, false, QR>), grid,
