@@ -88,14 +88,23 @@ def traffic_from_profiles(kernel_key):
 
 
 def launch_sequence(w):
-    """(kind, m, n) of every library launch of one step, in launch order."""
+    """(kind, m, n) of every library launch of one step, in launch order: per
+    oriented group (first appearance) and chunk of at most 64 matrices, prep,
+    norm, then gram, poly, update per Newton-Schulz step, the last update
+    being one final launch for the chunk's wide matrices and one for its tall
+    ones."""
+    groups = {}
+    for r, c in w.shapes:
+        groups.setdefault((min(r, c), max(r, c)), []).append(r > c)
     seq = []
-    for (m, n), cnt in w.oriented_groups().items():
-        for _ in range(0, cnt, 64):
+    for (m, n), talls in groups.items():
+        for b0 in range(0, len(talls), 64):
+            chunk = talls[b0:b0 + 64]
+            finals = [("final", m, n)] * ((not all(chunk)) + any(chunk))
             seq += [("prep", m, n), ("norm", m, n)]
             for k in range(w.n_steps):
-                seq += [("gram", m, n), ("poly", m, n),
-                        ("update" if k < w.n_steps - 1 else "final", m, n)]
+                seq += [("gram", m, n), ("poly", m, n)]
+                seq += [("update", m, n)] if k < w.n_steps - 1 else finals
     return seq
 
 

@@ -95,8 +95,9 @@ int muon_plan_groups(int n, const int* rows, const int* cols, int* group_of,
  *   in_dtype      MUON_BF16 or MUON_FP32; out_dtype likewise.
  *   coeffs        host, n_steps rows (copied during the call).
  *   eps           >= 0, finite (the step's default is 1e-7).
- *   compute       MUON_BF16: bf16 MFMA operands with fp32 accumulation and
- *                 an fp32 copy of X for the a*X term; MUON_FP32: fp32 throughout.
+ *   compute       MUON_BF16: bf16 MFMA operands with fp32 accumulation; X is
+ *                 carried between steps as two bf16 values (hi + lo, 16
+ *                 significant bits) for the a*X term; MUON_FP32: fp32 throughout.
  *   workspace     device, >= muon_orthogonalize_workspace_bytes(...) bytes,
  *                 MUON_WORKSPACE_ALIGN-aligned; contents on entry are ignored.
  * batch == 0 returns MUON_OK with nothing enqueued. */
