@@ -29,7 +29,10 @@ Parity pins: every function here is pinned by the tests in
 ``tests/test_oracle_pins.py`` (SVD closed form, convergence of the cubic
 iteration to U V^T, exact rational arithmetic on small integer matrices,
 tall/wide equivalence, orthogonal and scale invariance, closed forms for the
-momentum and update).  No function is "parity unpinned".
+momentum and update; for NorMuon the closed form on orthonormal rows, the
+RMS normalisation at beta2 = 0, the two-step EMA and transpose equivariance;
+for the cautious decay a hand-derived example and its special cases).  No
+function is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -106,6 +109,75 @@ def muon_step(w, grad, buf, mu: float, lr: float, scale: float, coeffs,
     new_buf, u = nesterov_momentum(grad, buf, mu)
     o = orthogonalize(u, coeffs, eps)
     return weight_update(w, o, lr, scale), new_buf, o
+
+
+# ---------------------------------------------------------------------------
+# Page 1, the paragraph after the Muon one, adds two things on top of the
+# plain step.  NorMuon: after orthogonalisation, per-row (or, by the aspect
+# ratio, per-column) second-moment estimates of the update, kept as an
+# exponential moving average, give every output dimension its own step size
+# (Adam's adaptivity applied in the orthogonalised coordinates).  Cautious
+# weight decay: only parameters whose update direction agrees in sign with
+# the parameter decay, mask = (update * param) >= 0.
+#
+# Readings where the page is silent (listed with reasons in the design
+# notes of the repository):
+#   * the statistics sit on the shorter side of the matrix: per row of a wide
+#     or square matrix, per column of a tall one (one value per row of the
+#     oriented matrix); the second moment is the mean of O^2 along the longer
+#     side;
+#   * v' = beta2*v + (1 - beta2)*mean(O^2), no bias correction; beta2 and the
+#     eps added to sqrt(v') are the caller's;
+#   * O' = O / (sqrt(v') + eps) broadcast along the longer side;
+#   * decoupled decay on the parameter before the update:
+#     W' = W - lr*scale*O' - lr*wd*mask*W, mask = (O'*W >= 0) when cautious,
+#     1 otherwise.
+
+
+def normuon_scale(o, v, beta2: float, eps: float):
+    """NorMuon scaling of an orthogonalised update O: returns (O', v').
+
+    ``v`` holds min(rows, cols) second moments, one per row of a wide or
+    square O, one per column of a tall O.
+    """
+    o = _f64(o)
+    v = _f64(v)
+    rows, cols = o.shape
+    axis = 0 if rows > cols else 1          # reduce along the longer side
+    msq = np.mean(o * o, axis=axis)
+    new_v = beta2 * v + (1.0 - beta2) * msq
+    d = np.sqrt(new_v) + eps
+    o_new = o / (d[None, :] if axis == 0 else d[:, None])
+    return o_new, new_v
+
+
+def decayed_weight_update(w, o, lr: float, scale: float, weight_decay: float,
+                          cautious: bool):
+    """W' = W - lr*scale*O - lr*weight_decay*mask*W, mask = (O*W >= 0) when
+    ``cautious`` (page 1's cautious weight decay), else 1 (plain decoupled
+    decay)."""
+    w = _f64(w)
+    o = _f64(o)
+    mask = (o * w >= 0.0) if cautious else np.ones_like(w, dtype=bool)
+    return w - lr * scale * o - lr * weight_decay * np.where(mask, w, 0.0)
+
+
+def muon_step_ex(w, grad, buf, mu: float, lr: float, scale: float, coeffs,
+                 eps: float = DEFAULT_EPS, weight_decay: float = 0.0,
+                 cautious: bool = True, second_moment=None, beta2: float = 0.0,
+                 normuon_eps: float = 0.0):
+    """The Muon step with page 1's additions: momentum, orthogonalisation,
+    NorMuon scaling (when ``second_moment`` is given), then the weight update
+    with (cautious) decoupled weight decay.  Returns a dict with ``w``,
+    ``buf``, ``o`` (the update direction applied) and ``v`` (the new second
+    moments, or None)."""
+    new_buf, u = nesterov_momentum(grad, buf, mu)
+    o = orthogonalize(u, coeffs, eps)
+    new_v = None
+    if second_moment is not None:
+        o, new_v = normuon_scale(o, second_moment, beta2, normuon_eps)
+    new_w = decayed_weight_update(w, o, lr, scale, weight_decay, cautious)
+    return {"w": new_w, "buf": new_buf, "o": o, "v": new_v}
 
 
 def relative_frobenius_error(y, y_ref) -> float:
