@@ -7,6 +7,11 @@ fraction of the dense bf16 MFMA peak / roofline of the dominant kernel /
 the fp64 oracle timed on the host cores as a CPU baseline.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--compute bf16|fp32]
+                    [--variant plain|cwd|normuon_cwd]
+
+--variant times muon_step_ex instead: page 1's cautious weight decay (cwd,
+decay 0.1) or NorMuon (beta2 0.95, eps 1e-8) with it (normuon_cwd).  The
+default, plain, is the benchmark's Muon step.
 """
 import argparse
 import gc
@@ -21,6 +26,12 @@ sys.path.insert(0, ROOT)
 PEAK = {"bf16": 2500.0, "fp32": 157.3}   # dense MFMA TFLOP/s, MI355X datasheet
 HBM_PEAK_GBS = 8000.0
 METRIC = "Muon step ms, 3.8B matrix set; NS TFLOP/s and % of bf16 MFMA peak"
+# muon_step_ex options of the non-default variants (the page gives no values)
+VARIANTS = {
+    "plain": None,
+    "cwd": dict(weight_decay=0.1, cautious=True),
+    "normuon_cwd": dict(weight_decay=0.1, cautious=True, beta2=0.95, normuon_eps=1e-8),
+}
 
 
 def parse():
@@ -30,6 +41,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="gpt_3.8b_28layers")
     p.add_argument("--compute", default="bf16", choices=["bf16", "fp32"])
+    p.add_argument("--variant", default="plain", choices=list(VARIANTS))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-seconds", type=float, default=12.0,
                    help="seconds of oracle work for the CPU baseline sample")
@@ -152,7 +164,7 @@ def write_traffic(fetch_csv, write_csv, w):
     print(f"wrote {TRAFFIC_JSON}")
 
 
-def cpu_baseline(w, seconds):
+def cpu_baseline(w, seconds, variant="plain"):
     """The fp64 oracle on a bounded sample of the workload: matrices taken
     round-robin over the oriented groups until about `seconds` of CPU work,
     per-group mean times extrapolated by the group counts."""
@@ -179,8 +191,17 @@ def cpu_baseline(w, seconds):
             g = x["grads"][0].double().numpy()
             b = x["bufs"][0].double().numpy()
             p = x["params"][0].double().numpy()
+            opt = VARIANTS[variant]
             t0 = time.perf_counter()
-            oracle.muon_step(p, g, b, w.mu, w.lr, x["scales"][0], w.coeff_table)
+            if opt is None:
+                oracle.muon_step(p, g, b, w.mu, w.lr, x["scales"][0], w.coeff_table)
+            else:
+                v = (wl.make_second_moment(w, idx).double().numpy()
+                     if "beta2" in opt else None)
+                oracle.muon_step_ex(p, g, b, w.mu, w.lr, x["scales"][0], w.coeff_table,
+                                    weight_decay=opt["weight_decay"], cautious=opt["cautious"],
+                                    second_moment=v, beta2=opt.get("beta2", 0.0),
+                                    normuon_eps=opt.get("normuon_eps", 0.0))
             dt = time.perf_counter() - t0
             times[key].append(dt)
             spent += dt
@@ -194,7 +215,8 @@ def cpu_baseline(w, seconds):
         "unit": "ms per step (extrapolated from the sample)",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"fp64 numpy Muon step on {sample} matrices (of {len(w.shapes)}), "
+        "sample": (f"fp64 numpy Muon step{'' if variant == 'plain' else ' (' + variant + ')'} "
+                   f"on {sample} matrices (of {len(w.shapes)}), "
                    f"{spent:.1f} s of CPU work; per-group mean x group count"),
     }
 
@@ -220,10 +242,20 @@ def main():
     torch.cuda.synchronize()
     ws = mn.Workspace()
 
+    opt = VARIANTS[args.variant]
+    vs = None
+    if opt is not None and "beta2" in opt:
+        vs = [wl.make_second_moment(w, i, device=dev) for i in range(len(w.shapes))]
+
     def one_step():
-        mn.step(inputs["params"], inputs["grads"], inputs["bufs"], mu=w.mu, lr=w.lr,
-                scales=inputs["scales"], coeffs=w.coeff_table, compute=args.compute,
-                workspace=ws)
+        if opt is None:
+            mn.step(inputs["params"], inputs["grads"], inputs["bufs"], mu=w.mu, lr=w.lr,
+                    scales=inputs["scales"], coeffs=w.coeff_table, compute=args.compute,
+                    workspace=ws)
+        else:
+            mn.step_ex(inputs["params"], inputs["grads"], inputs["bufs"], mu=w.mu, lr=w.lr,
+                       scales=inputs["scales"], coeffs=w.coeff_table, compute=args.compute,
+                       workspace=ws, second_moments=vs, **opt)
 
     if args.calibrate_copy:
         src = torch.ones(COPY_BYTES // 4, device=dev)
@@ -273,11 +305,11 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, args.cpu_sample_seconds)
+        cpu = cpu_baseline(w, args.cpu_sample_seconds, args.variant)
 
     groups = w.oriented_groups()
     out = {
-        "metric": METRIC,
+        "metric": METRIC if args.variant == "plain" else METRIC + f" ({args.variant})",
         "value": round(ms_per_step, 3),
         "unit": "ms",
         "n_gpus": 1,
@@ -289,7 +321,8 @@ def main():
         "vs_baseline": None,
         "dtype": args.compute,
         "data": "synthetic (seeded, generated on the GPU)",
-        "config": {"workload": w.name, "matrices": len(w.shapes),
+        "config": {"workload": w.name, "matrices": len(w.shapes), "variant": args.variant,
+                   **({"options": opt} if opt else {}),
                    "oriented_groups": {f"{m}x{n}": c for (m, n), c in groups.items()},
                    "ns_steps": w.n_steps, "coeffs": list(w.coeffs),
                    "parallelism": "single GPU (one GPU's share of a matrix-sharded step)"},

@@ -131,6 +131,55 @@ int muon_step(int n, const int* rows, const int* cols,
               const muon_coeff* coeffs, int n_steps, float eps, int compute,
               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Page 1, in the paragraph after the Muon one, adds two things on top of the
+ * plain step.  NorMuon: after orthogonalisation, per-row (or, by the aspect
+ * ratio, per-column) second-moment estimates of the update, kept as an
+ * exponential moving average, give each output dimension its own step size.
+ * Cautious weight decay: only parameters whose update direction agrees in
+ * sign with the parameter decay, mask = (update * param) >= 0.  The page
+ * gives no constants; this library takes them from the caller and reads:
+ *   - NorMuon statistics on the shorter side of the matrix (per row of a wide
+ *     or square matrix, per column of a tall one), the second moment being
+ *     the mean of O^2 along the longer side;
+ *     v' = beta2 * v + (1 - beta2) * mean(O^2), no bias correction;
+ *     O' = O / (sqrt(v') + normuon_eps);
+ *   - decoupled decay on the parameter before the update:
+ *     W' = W - lr*scale*O' - lr*weight_decay*mask*W, mask = (O'*W >= 0) when
+ *     cautious, 1 otherwise. */
+typedef struct {
+  float weight_decay;  /* finite, >= 0; 0 disables the decay */
+  int cautious;        /* 0 or 1 */
+  int normuon;         /* 0 or 1: NorMuon scaling with `second_moment` */
+  float beta2;         /* NorMuon EMA factor, in [0, 1] */
+  float normuon_eps;   /* NorMuon: finite, >= 0 */
+} muon_options;
+
+/* Workspace bytes of muon_step_ex for these shapes and options (NULL
+ * options: as muon_step_workspace_bytes).  0 for invalid sizes or n == 0. */
+size_t muon_step_ex_workspace_bytes(int n, const int* rows, const int* cols, int compute,
+                                    const muon_options* options);
+
+/* muon_step with page 1's additions.  Arguments as for muon_step, plus:
+ *   second_moment  host array of n device pointers, fp32, min(rows[i], cols[i])
+ *                  elements each, in/out (read and written only when
+ *                  options->normuon; may be NULL otherwise).  Each is
+ *                  4-byte aligned and overlaps none of params[i], grads[i],
+ *                  momentum[i].
+ *   options        NULL: exactly muon_step.
+ * For each matrix i: momentum and orthogonalisation as in muon_step, then
+ * (normuon) O' and v' as above, then the decayed weight update with O'.
+ * Invalid options (negative or non-finite weight_decay or normuon_eps,
+ * beta2 outside [0, 1], flags other than 0/1, missing second moments)
+ * return MUON_ERR_INVALID_ARG before anything is enqueued. */
+int muon_step_ex(int n, const int* rows, const int* cols,
+                 void* const* params, int param_dtype,
+                 const void* const* grads, int grad_dtype,
+                 float* const* momentum, float* const* second_moment,
+                 float mu, float lr, const float* scale,
+                 const muon_coeff* coeffs, int n_steps, float eps, int compute,
+                 const muon_options* options,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------ measurement */
 
 /* Kernel classes reported by the timing log. */
@@ -140,7 +189,9 @@ typedef enum {
   MUON_K_GRAM = 2,   /* A = X X^T, one triangle, mirrored */
   MUON_K_POLY = 3,   /* B = b A + c A^2 */
   MUON_K_UPDATE = 4, /* X <- a X + B X, steps before the last */
-  MUON_K_FINAL = 5   /* last step's a X + B X, written to the weights or output */
+  MUON_K_FINAL = 5,  /* last step's a X + B X, written to the weights or output */
+  MUON_K_NORMUON = 6, /* NorMuon row statistics and second-moment update */
+  MUON_K_APPLY = 7   /* weight update as its own pass (after NorMuon) */
 } muon_kernel_kind;
 
 typedef struct {

@@ -7,6 +7,7 @@ which PyTorch-ROCm exposes as ``torch.cuda.current_stream().cuda_stream``).
 
     orthogonalize(x, coeffs)                       -> O for one matrix or a batch
     step(params, grads, bufs, mu=, lr=, scales=, coeffs=)   in place
+    step_ex(..., weight_decay=, cautious=, second_moments=, beta2=, normuon_eps=)
 """
 from __future__ import annotations
 
@@ -166,6 +167,37 @@ def step(params, grads, bufs, *, mu, lr, scales=None, coeffs=QUINTIC, n_steps=No
          eps=DEFAULT_EPS, compute="bf16", workspace=None):
     """One Muon step, in place on ``params`` (fp32) and ``bufs`` (fp32
     momentum), for lists of 2-D GPU tensors of any mix of shapes."""
+    _step(params, grads, bufs, None, None, mu=mu, lr=lr, scales=scales, coeffs=coeffs,
+          n_steps=n_steps, eps=eps, compute=compute, workspace=workspace)
+
+
+def step_ex(params, grads, bufs, *, mu, lr, scales=None, coeffs=QUINTIC, n_steps=None,
+            eps=DEFAULT_EPS, compute="bf16", workspace=None, weight_decay=0.0,
+            cautious=True, second_moments=None, beta2=None, normuon_eps=None):
+    """``step`` with page 1's additions (muon_step_ex): decoupled weight decay
+    (cautious: only where update * param >= 0) and, when ``second_moments``
+    (fp32 vectors of min(rows, cols) elements, in place) are given, NorMuon
+    scaling with ``beta2`` and ``normuon_eps`` (no defaults: the page gives
+    none)."""
+    normuon = second_moments is not None
+    if normuon and (beta2 is None or normuon_eps is None):
+        raise ValueError("NorMuon needs beta2 and normuon_eps")
+    opt = _lib.MuonOptions(float(weight_decay), 1 if cautious else 0, 1 if normuon else 0,
+                           float(beta2) if normuon else 0.0,
+                           float(normuon_eps) if normuon else 0.0)
+    if normuon:
+        if len(second_moments) != len(params):
+            raise ValueError("one second-moment vector per matrix")
+        for p, v in zip(params, second_moments):
+            if (v.dtype != _torch().float32 or not v.is_contiguous()
+                    or v.numel() != min(p.shape)):
+                raise ValueError("second moments: contiguous fp32, min(rows, cols) elements")
+    _step(params, grads, bufs, second_moments, opt, mu=mu, lr=lr, scales=scales,
+          coeffs=coeffs, n_steps=n_steps, eps=eps, compute=compute, workspace=workspace)
+
+
+def _step(params, grads, bufs, second_moments, opt, *, mu, lr, scales, coeffs, n_steps, eps,
+          compute, workspace):
     n = len(params)
     if not (len(grads) == len(bufs) == n):
         raise ValueError("params, grads and bufs must have the same length")
@@ -188,18 +220,30 @@ def step(params, grads, bufs, *, mu, lr, scales=None, coeffs=QUINTIC, n_steps=No
     rows = _lib.int_array(r for r, _ in shapes)
     cols = _lib.int_array(c for _, c in shapes)
     c = _compute_code(compute)
-    need = int(lib().muon_step_workspace_bytes(n, rows, cols, c))
     device = params[0].device
-    wptr, wbytes = _workspace(need, device, workspace)
-    st = lib().muon_step(
-        n, rows, cols,
-        _lib.ptr_array(p.data_ptr() for p in params), _dtype_code(params[0].dtype),
-        _lib.ptr_array(g.data_ptr() for g in grads), grad_dtype,
-        _lib.ptr_array(b.data_ptr() for b in bufs),
-        float(mu), float(lr), _lib.float_array(scales), table, n_steps, float(eps), c,
-        ctypes.c_void_p(wptr), wbytes, _stream(device))
+    common = (_lib.ptr_array(p.data_ptr() for p in params), _dtype_code(params[0].dtype),
+              _lib.ptr_array(g.data_ptr() for g in grads), grad_dtype,
+              _lib.ptr_array(b.data_ptr() for b in bufs))
+    if opt is None:
+        need = int(lib().muon_step_workspace_bytes(n, rows, cols, c))
+        wptr, wbytes = _workspace(need, device, workspace)
+        st = lib().muon_step(
+            n, rows, cols, *common,
+            float(mu), float(lr), _lib.float_array(scales), table, n_steps, float(eps), c,
+            ctypes.c_void_p(wptr), wbytes, _stream(device))
+        where = "muon_step"
+    else:
+        need = int(lib().muon_step_ex_workspace_bytes(n, rows, cols, c, ctypes.byref(opt)))
+        wptr, wbytes = _workspace(need, device, workspace)
+        vptrs = (_lib.ptr_array(v.data_ptr() for v in second_moments)
+                 if second_moments is not None else None)
+        st = lib().muon_step_ex(
+            n, rows, cols, *common, vptrs,
+            float(mu), float(lr), _lib.float_array(scales), table, n_steps, float(eps), c,
+            ctypes.byref(opt), ctypes.c_void_p(wptr), wbytes, _stream(device))
+        where = "muon_step_ex"
     if st != MUON_OK:
-        raise MuonError(st, "muon_step")
+        raise MuonError(st, where)
 
 
 def timing_enable(on: bool = True) -> bool:

@@ -12,7 +12,7 @@ MUON_OK, MUON_ERR_INVALID_ARG, MUON_ERR_UNSUPPORTED, MUON_ERR_WORKSPACE, MUON_ER
 MUON_MAX_STEPS = 64
 MUON_WORKSPACE_ALIGN = 256
 MUON_PTR_ALIGN = 16
-KERNEL_KINDS = ("prep", "norm", "gram", "poly", "update", "final")
+KERNEL_KINDS = ("prep", "norm", "gram", "poly", "update", "final", "normuon", "apply")
 
 # Every symbol include/muon.h declares.
 EXPORTS = (
@@ -22,6 +22,8 @@ EXPORTS = (
     "muon_plan_groups",
     "muon_orthogonalize",
     "muon_step",
+    "muon_step_ex_workspace_bytes",
+    "muon_step_ex",
     "muon_timing_enable",
     "muon_timing_read",
 )
@@ -29,6 +31,12 @@ EXPORTS = (
 
 class MuonCoeff(ctypes.Structure):
     _fields_ = [("a", ctypes.c_float), ("b", ctypes.c_float), ("c", ctypes.c_float)]
+
+
+class MuonOptions(ctypes.Structure):
+    _fields_ = [("weight_decay", ctypes.c_float), ("cautious", ctypes.c_int),
+                ("normuon", ctypes.c_int), ("beta2", ctypes.c_float),
+                ("normuon_eps", ctypes.c_float)]
 
 
 class MuonTimingRecord(ctypes.Structure):
@@ -73,6 +81,16 @@ def load() -> ctypes.CDLL:
         ctypes.c_float, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(MuonCoeff),
         ctypes.c_int, ctypes.c_float, ctypes.c_int, _vp, ctypes.c_size_t, _vp]
     lib.muon_step.restype = ctypes.c_int
+    lib.muon_step_ex_workspace_bytes.argtypes = [ctypes.c_int, _c_int_p, _c_int_p, ctypes.c_int,
+                                                 ctypes.POINTER(MuonOptions)]
+    lib.muon_step_ex_workspace_bytes.restype = ctypes.c_size_t
+    lib.muon_step_ex.argtypes = [
+        ctypes.c_int, _c_int_p, _c_int_p, ctypes.POINTER(_vp), ctypes.c_int,
+        ctypes.POINTER(_vp), ctypes.c_int, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+        ctypes.c_float, ctypes.c_float, ctypes.POINTER(ctypes.c_float),
+        ctypes.POINTER(MuonCoeff), ctypes.c_int, ctypes.c_float, ctypes.c_int,
+        ctypes.POINTER(MuonOptions), _vp, ctypes.c_size_t, _vp]
+    lib.muon_step_ex.restype = ctypes.c_int
     lib.muon_timing_enable.argtypes = [ctypes.c_int]
     lib.muon_timing_enable.restype = ctypes.c_int
     lib.muon_timing_read.argtypes = [ctypes.POINTER(MuonTimingRecord), ctypes.c_int, _c_int_p]

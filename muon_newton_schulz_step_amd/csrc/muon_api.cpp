@@ -61,13 +61,14 @@ int pick_tile(bool cbf16, long long tiles_at_256, int batch) {
 // M x N), the X state as described for PrepArgs:
 //   bf16: hi plane twice (the update reads one, writes the other), lo plane;
 //   fp32: X, X^T twice (read by the update, written by it).
-// Then A and B (M x M, compute precision), the norm partials and 1/norm.
+// Then A and B (M x M, compute precision), the norm partials and 1/norm,
+// and with NorMuon the per-row scales 1/(sqrt(v') + eps) (M floats).
 struct Layout {
   int m = 0, n = 0, M = 0, N = 0, cnt = 0, nblk = 0;
-  size_t x0 = 0, x1 = 0, x2 = 0, A = 0, B = 0, part = 0, inv = 0, total = 0;
+  size_t x0 = 0, x1 = 0, x2 = 0, A = 0, B = 0, part = 0, inv = 0, rinv = 0, total = 0;
 };
 
-bool make_layout(int cnt, int m, int n, bool cbf16, Layout& L) {
+bool make_layout(int cnt, int m, int n, bool cbf16, Layout& L, bool normuon = false) {
   const long long M = pad_dim(m), N = pad_dim(n);
   if (M * N > MUON_MAX_ELEMENTS) return false;
   L.m = m; L.n = n; L.M = (int)M; L.N = (int)N; L.cnt = cnt;
@@ -87,6 +88,7 @@ bool make_layout(int cnt, int m, int n, bool cbf16, Layout& L) {
   L.B = take((size_t)cnt * MM * es);
   L.part = take((size_t)cnt * (size_t)L.nblk * 4);
   L.inv = take((size_t)cnt * 4);
+  if (normuon) L.rinv = take((size_t)cnt * (size_t)M * 4);
   L.total = off;
   return true;
 }
@@ -155,6 +157,11 @@ struct Chunk {
   void* out; long long s_out; int out_bf16;
   WeightTable wt;
   float neg_lr;
+  float neg_lrwd;                     // -lr * weight decay (0: none)
+  int cautious;
+  int normuon;                        // NorMuon after the last step
+  float beta2, eps2;
+  RowTable vt;                        // NorMuon second moments
 };
 
 int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeffs, int n_steps,
@@ -251,10 +258,14 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
     // tall matrices: runs of 4 elements of a stored row (length m) are
     // aligned when m and the output's matrix stride are multiples of 4
     g.vec_tall = L.m % 4 == 0 && (c.final_mode != FINAL_OUT || c.s_out % 4 == 0);
+    g.neg_lrwd = c.neg_lrwd;
+    g.cautious = c.cautious;
     // reads B and the operand X; the epilogue reads X (bf16: hi + lo, fp32:
     // X) and writes the next X (bf16: hi + lo, fp32: X + X^T), or, on the
     // last step, reads and writes the weights or writes the output
-    if (!last) {
+    if (!last || c.normuon) {
+      // (with NorMuon the last step is a plain update too; the weights
+      // follow in their own passes below)
       const double upd_bytes = pmm * es + pmn * es + pmn * 4.0 + pmn * (cbf16 ? 4.0 : 8.0);
       err = timed(MUON_K_UPDATE, L.m, L.n, c.cnt, k, cnt * 2.0 * m * m * n, upd_bytes, s,
                   [&] { return launch_gemm(cbf16, EPI_UPDATE, tile_upd, g, c.wt, c.cnt, s); });
@@ -280,6 +291,31 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
     }
     if (err != hipSuccess) return MUON_ERR_HIP;
   }
+  if (c.normuon) {
+    // O is the X state after the last step: hi plane n_steps % 2 (+ lo), or
+    // the fp32 X.  Row statistics and scales, then the weights.
+    float* rinv = reinterpret_cast<float*>(ws + L.rinv);
+    NormuonArgs na{};
+    na.m = L.m; na.n = L.n; na.M = L.M; na.N = L.N;
+    na.sX = MN; na.ldx = L.N;
+    na.Xh = Xh[n_steps & 1]; na.Xl = Xl; na.Xf = Xf;
+    na.beta2 = c.beta2; na.eps2 = c.eps2;
+    na.rinv = rinv;
+    err = timed(MUON_K_NORMUON, L.m, L.n, c.cnt, -1, 0.0, pmn * 4.0 + cnt * L.m * 8.0, s,
+                [&] { return launch_normuon_rows(cbf16, na, c.vt, c.cnt, s); });
+    if (err != hipSuccess) return MUON_ERR_HIP;
+    ApplyArgs aa{};
+    aa.m = L.m; aa.n = L.n; aa.M = L.M; aa.N = L.N;
+    aa.tall_mask = c.tall_mask;
+    aa.tiles_n = L.N / kPrepTile;
+    aa.sX = MN; aa.ldx = L.N;
+    aa.Xh = Xh[n_steps & 1]; aa.Xl = Xl; aa.Xf = Xf;
+    aa.rinv = rinv;
+    aa.neg_lr = c.neg_lr; aa.neg_lrwd = c.neg_lrwd; aa.cautious = c.cautious;
+    err = timed(MUON_K_APPLY, L.m, L.n, c.cnt, -1, 0.0, elems * 12.0, s,
+                [&] { return launch_apply(cbf16, aa, c.wt, c.cnt, s); });
+    if (err != hipSuccess) return MUON_ERR_HIP;
+  }
   return MUON_OK;
 }
 
@@ -300,6 +336,129 @@ bool shape_ok(int rows, int cols) {
 bool overlap(const void* p, size_t pb, const void* q, size_t qb) {
   const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
   return a < b + qb && b < a + pb;
+}
+
+size_t step_ws_bytes(int n, const int* rows, const int* cols, int compute, bool normuon) {
+  if (n < 1 || !rows || !cols || !is_dtype(compute)) return 0;
+  for (int i = 0; i < n; ++i)
+    if (!shape_ok(rows[i], cols[i])) return 0;
+  std::vector<Group> groups;
+  plan(n, rows, cols, groups, nullptr);
+  size_t best = 0;
+  for (const Group& g : groups) {
+    const int cnt = (int)g.idx.size() < kChunk ? (int)g.idx.size() : kChunk;
+    Layout L;
+    if (!make_layout(cnt, g.m, g.n, compute == MUON_BF16, L, normuon)) return 0;
+    if (L.total > best) best = L.total;
+  }
+  return best;
+}
+
+int check_options(const muon_options* o) {
+  if (!o) return MUON_OK;
+  if (!is_finite(o->weight_decay) || o->weight_decay < 0.f) return MUON_ERR_INVALID_ARG;
+  if ((o->cautious != 0 && o->cautious != 1) || (o->normuon != 0 && o->normuon != 1))
+    return MUON_ERR_INVALID_ARG;
+  if (o->normuon) {
+    if (!is_finite(o->beta2) || o->beta2 < 0.f || o->beta2 > 1.f) return MUON_ERR_INVALID_ARG;
+    if (!is_finite(o->normuon_eps) || o->normuon_eps < 0.f) return MUON_ERR_INVALID_ARG;
+  }
+  return MUON_OK;
+}
+
+// muon_step and muon_step_ex (opt == nullptr: the plain step).
+int step_impl(int n, const int* rows, const int* cols, void* const* params, int param_dtype,
+              const void* const* grads, int grad_dtype, float* const* momentum,
+              float* const* second_moment, float mu, float lr, const float* scale,
+              const muon_coeff* coeffs, int n_steps, float eps, int compute,
+              const muon_options* opt, void* workspace, size_t workspace_bytes,
+              hipStream_t stream) {
+  if (n < 0) return MUON_ERR_INVALID_ARG;
+  if (!is_dtype(param_dtype) || !is_dtype(grad_dtype) || !is_dtype(compute))
+    return MUON_ERR_INVALID_ARG;
+  if (int st = check_coeffs(coeffs, n_steps, eps)) return st;
+  if (!is_finite(mu) || !is_finite(lr)) return MUON_ERR_INVALID_ARG;
+  if (int st = check_options(opt)) return st;
+  const bool normuon = opt && opt->normuon;
+  if (n == 0) return MUON_OK;
+  if (!rows || !cols || !params || !grads || !momentum || !scale) return MUON_ERR_INVALID_ARG;
+  if (normuon && !second_moment) return MUON_ERR_INVALID_ARG;
+  const size_t gsz = grad_dtype == MUON_BF16 ? 2 : 4;
+  for (int i = 0; i < n; ++i) {
+    if (!shape_ok(rows[i], cols[i])) return MUON_ERR_INVALID_ARG;
+    if (!params[i] || !grads[i] || !momentum[i]) return MUON_ERR_INVALID_ARG;
+    if (!aligned(params[i], MUON_PTR_ALIGN) || !aligned(grads[i], MUON_PTR_ALIGN) ||
+        !aligned(momentum[i], MUON_PTR_ALIGN))
+      return MUON_ERR_INVALID_ARG;
+    if (!is_finite(scale[i])) return MUON_ERR_INVALID_ARG;
+    const size_t el = (size_t)rows[i] * cols[i];
+    if (overlap(params[i], el * 4, grads[i], el * gsz) ||
+        overlap(params[i], el * 4, momentum[i], el * 4) ||
+        overlap(grads[i], el * gsz, momentum[i], el * 4))
+      return MUON_ERR_INVALID_ARG;
+    if (normuon) {
+      const void* v = second_moment[i];
+      const size_t vb = (size_t)(rows[i] < cols[i] ? rows[i] : cols[i]) * 4;
+      if (!v || !aligned(v, 4)) return MUON_ERR_INVALID_ARG;
+      if (overlap(v, vb, params[i], el * 4) || overlap(v, vb, grads[i], el * gsz) ||
+          overlap(v, vb, momentum[i], el * 4))
+        return MUON_ERR_INVALID_ARG;
+    }
+  }
+  if (param_dtype != MUON_FP32) return MUON_ERR_UNSUPPORTED;
+  const size_t need = step_ws_bytes(n, rows, cols, compute, normuon);
+  if (need == 0) return MUON_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < need || !aligned(workspace, kWsAlign))
+    return MUON_ERR_WORKSPACE;
+
+  const bool cbf16 = compute == MUON_BF16;
+  std::vector<Group> groups;
+  plan(n, rows, cols, groups, nullptr);
+  char* ws = static_cast<char*>(workspace);
+  for (const Group& g : groups) {
+    const int total = (int)g.idx.size();
+    for (int b0 = 0; b0 < total; b0 += kChunk) {
+      const int cnt = total - b0 < kChunk ? total - b0 : kChunk;
+      // Tall and wide matrices of one oriented shape share the launch: the
+      // kernels read each matrix's orientation from the mask.
+      Chunk c{};
+      // wide matrices first, then the tall ones (the last step launches the
+      // two orientations separately, each over a contiguous range)
+      int order[kChunk];
+      int no = 0;
+      for (int pass = 0; pass < 2; ++pass)
+        for (int q = 0; q < cnt; ++q) {
+          const int i = g.idx[b0 + q];
+          if ((rows[i] > cols[i]) == (pass == 1)) order[no++] = i;
+        }
+      for (int q = 0; q < cnt; ++q) {
+        const int i = order[q];
+        c.pt.g[q] = grads[i];
+        c.pt.buf[q] = momentum[i];
+        c.wt.w[q] = static_cast<float*>(params[i]);
+        c.wt.scale[q] = scale[i];
+        if (normuon) c.vt.v[q] = second_moment[i];
+        if (rows[i] > cols[i]) c.tall_mask |= 1ull << q;
+      }
+      Layout L;
+      make_layout(cnt, g.m, g.n, cbf16, L, normuon);
+      c.cnt = cnt;
+      c.momentum = true;
+      c.in_bf16 = grad_dtype == MUON_BF16;
+      c.mu = mu;
+      c.final_mode = FINAL_WEIGHTS;
+      c.neg_lr = -lr;
+      if (opt) {
+        c.neg_lrwd = -lr * opt->weight_decay;
+        c.cautious = opt->cautious;
+        c.normuon = opt->normuon;
+        c.beta2 = opt->beta2;
+        c.eps2 = opt->normuon_eps;
+      }
+      if (int st = run_chunk(c, L, ws, coeffs, n_steps, eps, cbf16, stream)) return st;
+    }
+  }
+  return MUON_OK;
 }
 
 }  // namespace
@@ -327,19 +486,13 @@ size_t muon_orthogonalize_workspace_bytes(int batch, int rows, int cols, int com
 }
 
 size_t muon_step_workspace_bytes(int n, const int* rows, const int* cols, int compute) {
-  if (n < 1 || !rows || !cols || !is_dtype(compute)) return 0;
-  for (int i = 0; i < n; ++i)
-    if (!shape_ok(rows[i], cols[i])) return 0;
-  std::vector<Group> groups;
-  plan(n, rows, cols, groups, nullptr);
-  size_t best = 0;
-  for (const Group& g : groups) {
-    const int cnt = (int)g.idx.size() < kChunk ? (int)g.idx.size() : kChunk;
-    Layout L;
-    if (!make_layout(cnt, g.m, g.n, compute == MUON_BF16, L)) return 0;
-    if (L.total > best) best = L.total;
-  }
-  return best;
+  return step_ws_bytes(n, rows, cols, compute, false);
+}
+
+size_t muon_step_ex_workspace_bytes(int n, const int* rows, const int* cols, int compute,
+                                    const muon_options* options) {
+  if (check_options(options) != MUON_OK) return 0;
+  return step_ws_bytes(n, rows, cols, compute, options && options->normuon);
 }
 
 int muon_plan_groups(int n, const int* rows, const int* cols, int* group_of, int* group_m,
@@ -413,73 +566,20 @@ int muon_step(int n, const int* rows, const int* cols, void* const* params, int 
               const void* const* grads, int grad_dtype, float* const* momentum, float mu,
               float lr, const float* scale, const muon_coeff* coeffs, int n_steps, float eps,
               int compute, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (n < 0) return MUON_ERR_INVALID_ARG;
-  if (!is_dtype(param_dtype) || !is_dtype(grad_dtype) || !is_dtype(compute))
-    return MUON_ERR_INVALID_ARG;
-  if (int st = check_coeffs(coeffs, n_steps, eps)) return st;
-  if (!is_finite(mu) || !is_finite(lr)) return MUON_ERR_INVALID_ARG;
-  if (n == 0) return MUON_OK;
-  if (!rows || !cols || !params || !grads || !momentum || !scale) return MUON_ERR_INVALID_ARG;
-  const size_t gsz = grad_dtype == MUON_BF16 ? 2 : 4;
-  for (int i = 0; i < n; ++i) {
-    if (!shape_ok(rows[i], cols[i])) return MUON_ERR_INVALID_ARG;
-    if (!params[i] || !grads[i] || !momentum[i]) return MUON_ERR_INVALID_ARG;
-    if (!aligned(params[i], MUON_PTR_ALIGN) || !aligned(grads[i], MUON_PTR_ALIGN) ||
-        !aligned(momentum[i], MUON_PTR_ALIGN))
-      return MUON_ERR_INVALID_ARG;
-    if (!is_finite(scale[i])) return MUON_ERR_INVALID_ARG;
-    const size_t el = (size_t)rows[i] * cols[i];
-    if (overlap(params[i], el * 4, grads[i], el * gsz) ||
-        overlap(params[i], el * 4, momentum[i], el * 4) ||
-        overlap(grads[i], el * gsz, momentum[i], el * 4))
-      return MUON_ERR_INVALID_ARG;
-  }
-  if (param_dtype != MUON_FP32) return MUON_ERR_UNSUPPORTED;
-  const size_t need = muon_step_workspace_bytes(n, rows, cols, compute);
-  if (need == 0) return MUON_ERR_INVALID_ARG;
-  if (!workspace || workspace_bytes < need || !aligned(workspace, kWsAlign))
-    return MUON_ERR_WORKSPACE;
+  return step_impl(n, rows, cols, params, param_dtype, grads, grad_dtype, momentum, nullptr, mu,
+                   lr, scale, coeffs, n_steps, eps, compute, nullptr, workspace,
+                   workspace_bytes, stream);
+}
 
-  const bool cbf16 = compute == MUON_BF16;
-  std::vector<Group> groups;
-  plan(n, rows, cols, groups, nullptr);
-  char* ws = static_cast<char*>(workspace);
-  for (const Group& g : groups) {
-    const int total = (int)g.idx.size();
-    for (int b0 = 0; b0 < total; b0 += kChunk) {
-      const int cnt = total - b0 < kChunk ? total - b0 : kChunk;
-      // Tall and wide matrices of one oriented shape share the launch: the
-      // kernels read each matrix's orientation from the mask.
-      Chunk c{};
-      // wide matrices first, then the tall ones (the last step launches the
-      // two orientations separately, each over a contiguous range)
-      int order[kChunk];
-      int no = 0;
-      for (int pass = 0; pass < 2; ++pass)
-        for (int q = 0; q < cnt; ++q) {
-          const int i = g.idx[b0 + q];
-          if ((rows[i] > cols[i]) == (pass == 1)) order[no++] = i;
-        }
-      for (int q = 0; q < cnt; ++q) {
-        const int i = order[q];
-        c.pt.g[q] = grads[i];
-        c.pt.buf[q] = momentum[i];
-        c.wt.w[q] = static_cast<float*>(params[i]);
-        c.wt.scale[q] = scale[i];
-        if (rows[i] > cols[i]) c.tall_mask |= 1ull << q;
-      }
-      Layout L;
-      make_layout(cnt, g.m, g.n, cbf16, L);
-      c.cnt = cnt;
-      c.momentum = true;
-      c.in_bf16 = grad_dtype == MUON_BF16;
-      c.mu = mu;
-      c.final_mode = FINAL_WEIGHTS;
-      c.neg_lr = -lr;
-      if (int st = run_chunk(c, L, ws, coeffs, n_steps, eps, cbf16, stream)) return st;
-    }
-  }
-  return MUON_OK;
+int muon_step_ex(int n, const int* rows, const int* cols, void* const* params, int param_dtype,
+                 const void* const* grads, int grad_dtype, float* const* momentum,
+                 float* const* second_moment, float mu, float lr, const float* scale,
+                 const muon_coeff* coeffs, int n_steps, float eps, int compute,
+                 const muon_options* options, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream) {
+  return step_impl(n, rows, cols, params, param_dtype, grads, grad_dtype, momentum,
+                   second_moment, mu, lr, scale, coeffs, n_steps, eps, compute, options,
+                   workspace, workspace_bytes, stream);
 }
 
 int muon_timing_enable(int on) { return g_timing.exchange(on ? 1 : 0); }

@@ -81,6 +81,8 @@ struct GemmArgs {
   void* out; long long s_out; int out_bf16;
   int vec_tall;            // FINAL of tall matrices: 4 consecutive i of a
                            // weight / output row are 16- (8-) byte aligned
+  float neg_lrwd;          // FINAL_W: -lr * weight_decay (0: no decay)
+  int cautious;            // FINAL_W: decay only where O * W >= 0
   float neg_lr;
 };
 
@@ -100,6 +102,44 @@ struct GemmLaunch {
   WeightTable wt;
 };
 
+// NorMuon: per oriented row i of the final X (= O, m x n), in fixed order,
+// s = sum_j O[i][j]^2, v[i] <- beta2 v[i] + (1 - beta2) s / n and
+// rinv[i] = 1 / (sqrt(v[i]) + eps2) (0 for padding rows).
+struct RowTable {          // per-matrix second-moment vectors, m floats each
+  float* v[kChunk];
+};
+struct NormuonArgs {
+  int m, n, M, N;
+  long long sX; int ldx;   // X state as in GemmArgs
+  const void* Xh; const void* Xl;  // bf16: hi, lo
+  const float* Xf;                 // fp32: X
+  float beta2, eps2;
+  float* rinv;             // [matrix][M]
+};
+struct NormuonLaunch {
+  NormuonArgs a;
+  RowTable t;
+};
+
+// The weight update as its own pass (after NorMuon): per element of W in
+// the caller's orientation, with O from the oriented X state,
+//   W <- W - lr*scale*O*rinv[i] - lr*wd*mask*W,  mask = (O*W >= 0) if cautious.
+struct ApplyArgs {
+  int m, n, M, N;
+  unsigned long long tall_mask;
+  int tiles_n;             // N / kPrepTile
+  long long sX; int ldx;
+  const void* Xh; const void* Xl; const float* Xf;
+  const float* rinv;       // [matrix][M]
+  float neg_lr;            // -lr
+  float neg_lrwd;          // -lr * weight_decay
+  int cautious;
+};
+struct ApplyLaunch {
+  ApplyArgs a;
+  WeightTable wt;
+};
+
 // Launchers (return hipGetLastError() of the launch).
 hipError_t launch_prep(int grad_bf16, int compute_bf16, int momentum,
                        const PrepArgs& a, const PrepTable& t, int batch,
@@ -111,5 +151,9 @@ hipError_t launch_norm(const float* partials, int nblk, float eps, float* inv,
 int gemm_tile(int compute_bf16, int tile_pref);
 hipError_t launch_gemm(int compute_bf16, int epi, int tile, const GemmArgs& a,
                        const WeightTable& t, int batch, hipStream_t s);
+hipError_t launch_normuon_rows(int compute_bf16, const NormuonArgs& a, const RowTable& t,
+                               int batch, hipStream_t s);
+hipError_t launch_apply(int compute_bf16, const ApplyArgs& a, const WeightTable& t,
+                        int batch, hipStream_t s);
 
 }  // namespace muon

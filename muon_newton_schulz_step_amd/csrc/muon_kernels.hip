@@ -61,6 +61,18 @@ __device__ __forceinline__ void split_bf16(float x, bf16_t& hi, bf16_t& lo) {
   lo = from_f32<bf16_t>(x - to_f32(hi));
 }
 
+// One weight element: W' = W + wscale*x (wscale = -lr*scale, x the update
+// direction), minus lr*wd*W where the decay applies: everywhere, or with
+// page 1's cautious decay only where x*W >= 0.  neg_lrwd = -lr*wd; with 0
+// the decay term is skipped (so that non-finite weights propagate as in the
+// plain update).
+__device__ __forceinline__ float weight_step(float w, float x, float wscale, float neg_lrwd,
+                                             int cautious) {
+  const float nw = fmaf(wscale, x, w);
+  const bool decay = neg_lrwd != 0.f && (!cautious || x * w >= 0.f);
+  return decay ? fmaf(neg_lrwd, w, nw) : nw;
+}
+
 // Compile-time loop: f(std::integral_constant<int, 0>) ... f(<N-1>), so that
 // register arrays are never indexed at run time (which would put them in
 // scratch memory).
@@ -765,7 +777,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
             for (int s = 0; s < HALF; ++s) {
               f32x4_t w;
 #pragma unroll
-              for (int t = 0; t < 4; ++t) w[t] = fmaf(wscale, xv[s][t], wv[s][t]);
+              for (int t = 0; t < 4; ++t)
+              w[t] = weight_step(wv[s][t], xv[s][t], wscale, a.neg_lrwd, a.cautious);
               if (a.vec_tall && nval[s] == 4) {
                 *reinterpret_cast<f32x4_t*>(W + off[s]) = w;
               } else {
@@ -878,7 +891,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
             if (i < a.m && j < a.n) {
               const long long oo = tall ? (long long)j * a.m + i : (long long)i * a.n + j;
               if constexpr (FIN_W) {
-                W[oo] = fmaf(wscale, x, win[nn][e]);
+                W[oo] = weight_step(win[nn][e], x, wscale, a.neg_lrwd, a.cautious);
               } else if (a.out_bf16) {
                 static_cast<bf16_t*>(a.out)[(long long)mat * a.s_out + oo] = from_f32<bf16_t>(x);
               } else {
@@ -930,6 +943,108 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
   }
 }
 
+// ---------------------------------------------------------------- NorMuon
+// One block per oriented row i of the final X (= O) of each matrix: the sum
+// of O[i][j]^2 over the row (fixed order: per-thread strided partials, wave
+// butterfly, the four waves in order), then the second-moment update and
+// the row's scale 1/(sqrt(v') + eps2).  Padding rows (i >= m) get scale 0.
+template <bool HILO>
+__global__ __launch_bounds__(256) void normuon_rows_kernel(NormuonLaunch launch) {
+  const NormuonArgs& a = launch.a;
+  __shared__ float red[4];
+  const int i = blockIdx.x, mat = blockIdx.y, tid = threadIdx.x;
+  const long long row = (long long)mat * a.sX + (long long)i * a.ldx;
+  float s = 0.f;
+  if constexpr (HILO) {
+    const bf16_t* h = static_cast<const bf16_t*>(a.Xh) + row;
+    const bf16_t* l = static_cast<const bf16_t*>(a.Xl) + row;
+    for (int j = 8 * tid; j < a.N; j += 8 * 256) {
+      const bf16x8_t hv = *reinterpret_cast<const bf16x8_t*>(h + j);
+      const bf16x8_t lv = *reinterpret_cast<const bf16x8_t*>(l + j);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = to_f32(hv[e]) + to_f32(lv[e]);
+        s = fmaf(x, x, s);
+      }
+    }
+  } else {
+    const float* f = a.Xf + row;
+    for (int j = 4 * tid; j < a.N; j += 4 * 256) {
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(f + j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s = fmaf(v[e], v[e], s);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+  if ((tid & 63) == 0) red[tid >> 6] = s;
+  __syncthreads();
+  if (tid == 0) {
+    float r = 0.f;
+    if (i < a.m) {
+      const float total = (red[0] + red[1]) + (red[2] + red[3]);
+      float* v = kernarg<NormuonLaunch>().t.v[mat];
+      const float nv = a.beta2 * v[i] + (1.f - a.beta2) * (total / (float)a.n);
+      v[i] = nv;
+      r = 1.f / (sqrtf(nv) + a.eps2);
+    }
+    a.rinv[(long long)mat * a.M + i] = r;
+  }
+}
+
+// The weight update as its own pass: one 64x64 tile of the oriented, padded
+// M x N space per block, like prep_kernel in reverse.  O*rinv[i] is read
+// coalesced along the oriented rows; a tall matrix's weights (stored
+// transposed to the oriented X) are updated through a transposing LDS tile.
+template <bool HILO>
+__global__ __launch_bounds__(256) void apply_kernel(ApplyLaunch launch) {
+  const ApplyArgs& a = launch.a;
+  __shared__ float tile[kPrepTile][kPrepTile + 1];
+  const int tid = threadIdx.x, mat = blockIdx.y, bt = blockIdx.x;
+  const int oi0 = (bt / a.tiles_n) * kPrepTile;
+  const int oj0 = (bt % a.tiles_n) * kPrepTile;
+  const bool tall = (a.tall_mask >> mat) & 1ull;
+  float* __restrict__ W = kernarg<ApplyLaunch>().wt.w[mat];
+  const float wscale = a.neg_lr * kernarg<ApplyLaunch>().wt.scale[mat];
+  const float* rinv = a.rinv + (long long)mat * a.M;
+  const long long base = (long long)mat * a.sX;
+  auto o_at = [&](int oi, int oj) {
+    const long long o = base + (long long)oi * a.ldx + oj;
+    float x;
+    if constexpr (HILO) {
+      x = to_f32(static_cast<const bf16_t*>(a.Xh)[o]) + to_f32(static_cast<const bf16_t*>(a.Xl)[o]);
+    } else {
+      x = a.Xf[o];
+    }
+    return x * rinv[oi];
+  };
+  const int cc = tid & 63, rr = tid >> 6;
+  if (!tall) {
+#pragma unroll 4
+    for (int p = 0; p < kPrepTile / 4; ++p) {
+      const int oi = oi0 + rr + 4 * p, oj = oj0 + cc;  // = original (row, col)
+      if (oi < a.m && oj < a.n) {
+        const float x = o_at(oi, oj);
+        const long long idx = (long long)oi * a.n + oj;
+        W[idx] = weight_step(W[idx], x, wscale, a.neg_lrwd, a.cautious);
+      }
+    }
+  } else {
+#pragma unroll 4
+    for (int p = 0; p < kPrepTile / 4; ++p) tile[rr + 4 * p][cc] = o_at(oi0 + rr + 4 * p, oj0 + cc);
+    __syncthreads();
+#pragma unroll 4
+    for (int p = 0; p < kPrepTile / 4; ++p) {
+      const int lc = rr + 4 * p;
+      const int r = oj0 + lc, c = oi0 + cc;  // original (row, col) of oriented (c, r)
+      if (r < a.n && c < a.m) {
+        const long long idx = (long long)r * a.m + c;
+        W[idx] = weight_step(W[idx], tile[cc][lc], wscale, a.neg_lrwd, a.cautious);
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 hipError_t launch_prep(int grad_bf16, int compute_bf16, int momentum, const PrepArgs& a,
                        const PrepTable& t, int batch, hipStream_t s) {
@@ -957,6 +1072,27 @@ hipError_t launch_prep(int grad_bf16, int compute_bf16, int momentum, const Prep
 hipError_t launch_norm(const float* partials, int nblk, float eps, float* inv, int batch,
                        hipStream_t s) {
   hipLaunchKernelGGL(norm_kernel, dim3(batch), dim3(256), 0, s, partials, nblk, eps, inv);
+  return hipGetLastError();
+}
+
+hipError_t launch_normuon_rows(int compute_bf16, const NormuonArgs& a, const RowTable& t,
+                               int batch, hipStream_t s) {
+  const NormuonLaunch launch{a, t};
+  if (compute_bf16)
+    hipLaunchKernelGGL(normuon_rows_kernel<true>, dim3(a.M, batch), dim3(256), 0, s, launch);
+  else
+    hipLaunchKernelGGL(normuon_rows_kernel<false>, dim3(a.M, batch), dim3(256), 0, s, launch);
+  return hipGetLastError();
+}
+
+hipError_t launch_apply(int compute_bf16, const ApplyArgs& a, const WeightTable& t, int batch,
+                        hipStream_t s) {
+  const ApplyLaunch launch{a, t};
+  const dim3 grid((a.M / kPrepTile) * a.tiles_n, batch);
+  if (compute_bf16)
+    hipLaunchKernelGGL(apply_kernel<true>, grid, dim3(256), 0, s, launch);
+  else
+    hipLaunchKernelGGL(apply_kernel<false>, grid, dim3(256), 0, s, launch);
   return hipGetLastError();
 }
 

@@ -118,6 +118,69 @@ def test_step_rejects_before_enqueue(kw, expect):
     assert step_call(**kw) == expect
 
 
+def step_ex_call(n=2, rows=(8, 16), cols=(16, 8), vs=None, opt=None, ws=FAKE * 4096,
+                 ws_bytes=None, no_opt=False, no_vs=False):
+    lib = mn.lib()
+    params = [FAKE * (i + 1) * 64 for i in range(n)]
+    grads = [FAKE * (i + 1) * 64 + 4096 for i in range(n)]
+    bufs = [FAKE * (i + 1) * 64 + 8192 for i in range(n)]
+    if vs is None:
+        vs = [FAKE * (i + 1) * 64 + 16384 for i in range(n)]
+    if opt is None:
+        opt = dict(weight_decay=0.1, cautious=1, normuon=1, beta2=0.95, normuon_eps=1e-8)
+    o = _lib.MuonOptions(**opt)
+    r, c = _lib.int_array(rows), _lib.int_array(cols)
+    if ws_bytes is None:
+        ws_bytes = lib.muon_step_ex_workspace_bytes(n, r, c, 0, ctypes.byref(o)) if n > 0 else 0
+    return lib.muon_step_ex(
+        n, r, c, _lib.ptr_array(params), 1, _lib.ptr_array(grads), 0, _lib.ptr_array(bufs),
+        None if no_vs else _lib.ptr_array(vs), 0.95, 0.02, _lib.float_array([1.0] * n),
+        _lib.coeff_array(Q), 5, 1e-7, 0, None if no_opt else ctypes.byref(o),
+        ctypes.c_void_p(ws), ws_bytes, None)
+
+
+OPT = dict(weight_decay=0.1, cautious=1, normuon=1, beta2=0.95, normuon_eps=1e-8)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(n=0), mn.MUON_OK),
+    (dict(opt={**OPT, "weight_decay": -0.1}), mn.MUON_ERR_INVALID_ARG),
+    (dict(opt={**OPT, "weight_decay": float("nan")}), mn.MUON_ERR_INVALID_ARG),
+    (dict(opt={**OPT, "cautious": 2}), mn.MUON_ERR_INVALID_ARG),
+    (dict(opt={**OPT, "normuon": -1}), mn.MUON_ERR_INVALID_ARG),
+    (dict(opt={**OPT, "beta2": 1.5}), mn.MUON_ERR_INVALID_ARG),
+    (dict(opt={**OPT, "beta2": float("nan")}), mn.MUON_ERR_INVALID_ARG),
+    (dict(opt={**OPT, "normuon_eps": -1.0}), mn.MUON_ERR_INVALID_ARG),
+    (dict(opt={**OPT, "normuon_eps": float("inf")}), mn.MUON_ERR_INVALID_ARG),
+    (dict(no_vs=True), mn.MUON_ERR_INVALID_ARG),                    # NorMuon without buffers
+    (dict(vs=[FAKE * 64 + 16384, 0]), mn.MUON_ERR_INVALID_ARG),     # one missing
+    (dict(vs=[FAKE * 64 + 16386, FAKE * 128 + 16384]), mn.MUON_ERR_INVALID_ARG),  # misaligned
+    (dict(vs=[FAKE * 64 + 8, FAKE * 128 + 16384]), mn.MUON_ERR_INVALID_ARG),      # overlaps W
+    (dict(ws=0), mn.MUON_ERR_WORKSPACE),
+])
+def test_step_ex_rejects_before_enqueue(kw, expect):
+    assert step_ex_call(**kw) == expect
+
+
+def test_step_ex_workspace_sizes():
+    lib = mn.lib()
+    rows, cols = (3072, 1024, 12288), (12288, 3072, 3072)
+    r, c = _lib.int_array(rows), _lib.int_array(cols)
+    plain = lib.muon_step_workspace_bytes(3, r, c, 0)
+    assert lib.muon_step_ex_workspace_bytes(3, r, c, 0, None) == plain
+    wd_only = _lib.MuonOptions(0.1, 1, 0, 0.0, 0.0)
+    assert lib.muon_step_ex_workspace_bytes(3, r, c, 0, ctypes.byref(wd_only)) == plain
+    nm = _lib.MuonOptions(0.0, 1, 1, 0.9, 1e-8)
+    # NorMuon adds the per-row scales of the largest group: 2 x (3072, 12288)
+    # (one wide, one tall), 3072 floats each, 256-byte aligned
+    assert lib.muon_step_ex_workspace_bytes(3, r, c, 0, ctypes.byref(nm)) == plain + 2 * 3072 * 4
+    bad = _lib.MuonOptions(-1.0, 1, 0, 0.0, 0.0)
+    assert lib.muon_step_ex_workspace_bytes(3, r, c, 0, ctypes.byref(bad)) == 0
+    # with NorMuon the plain size is too small
+    assert step_ex_call(ws_bytes=lib.muon_step_workspace_bytes(
+        2, _lib.int_array((8, 16)), _lib.int_array((16, 8)), 0)) == mn.MUON_ERR_WORKSPACE
+
+
 def test_workspace_sizes():
     lib = mn.lib()
     small = lib.muon_orthogonalize_workspace_bytes(1, 256, 128, 0)

@@ -1,0 +1,114 @@
+"""muon_step_ex on the GPU vs the fp64 oracle: page 1's cautious weight
+decay and NorMuon scaling on top of the plain step, mixed shapes (tall,
+wide, square, ragged), both compute precisions, and the second-moment
+moving average carried over two steps.
+
+The cautious mask is a sign decision on O'*W.  Where |O'| lies within the
+arithmetic's error of zero both decisions are correct; there the comparison
+takes the oracle's value for whichever decision the GPU made, and the
+magnitude part (-lr*scale*O') is still compared.  Everywhere else the mask
+must agree."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import muon_newton_schulz_step_amd as mn
+import oracle
+import workloads as wl
+from gpu_helpers import BUF_TOL, announce, to64, tol
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+SHAPES = ((64, 128), (128, 64), (100, 300), (300, 100), (64, 64), (1, 5), (5, 1),
+          (257, 129), (64, 128), (256, 768), (768, 256))
+
+
+def expected_dw(ref, w_before, dw_gpu, lr, scale, wd, cautious, margin):
+    """Oracle dW with the cautious mask taken from the GPU where |O'| is below
+    ``margin`` (both decisions valid there)."""
+    o, w = ref["o"], w_before
+    dw_keep = -lr * scale * o
+    dw_decay = dw_keep - lr * wd * w
+    if not cautious:
+        return dw_decay
+    mask = o * w >= 0
+    dw = np.where(mask, dw_decay, dw_keep)
+    amb = np.abs(o) <= margin
+    closer = np.where(np.abs(dw_gpu - dw_decay) <= np.abs(dw_gpu - dw_keep), dw_decay, dw_keep)
+    return np.where(amb, closer, dw)
+
+
+def run_case(compute, wd, cautious, normuon, steps=1, shapes=SHAPES, beta2=0.9,
+             normuon_eps=1e-8):
+    announce("step_ex", compute, wd, cautious, normuon, steps)
+    w = dataclasses.replace(wl.GPT_D768, shapes=shapes)
+    inp = wl.make_inputs(w, device=DEV)
+    vs = [wl.make_second_moment(w, i, device=DEV) for i in range(len(shapes))] if normuon else None
+    state = [dict(w=to64(inp["params"][k]), buf=to64(inp["bufs"][k]),
+                  v=to64(vs[k]) if normuon else None) for k in range(len(shapes))]
+    for step in range(steps):
+        before = [to64(p) for p in inp["params"]]
+        mn.step_ex(inp["params"], inp["grads"], inp["bufs"], mu=w.mu, lr=w.lr,
+                   scales=inp["scales"], coeffs=w.coeff_table, compute=compute,
+                   weight_decay=wd, cautious=cautious, second_moments=vs,
+                   beta2=beta2 if normuon else None,
+                   normuon_eps=normuon_eps if normuon else None)
+        torch.cuda.synchronize()
+        for k, shape in enumerate(shapes):
+            g = to64(inp["grads"][k])
+            st = state[k]
+            ref = oracle.muon_step_ex(before[k], g, st["buf"], w.mu, w.lr, inp["scales"][k],
+                                      w.coeff_table, weight_decay=wd, cautious=cautious,
+                                      second_moment=st["v"] if normuon else None,
+                                      beta2=beta2, normuon_eps=normuon_eps)
+            t = tol(compute, shape)
+            dw_gpu = to64(inp["params"][k]) - before[k]
+            rms = float(np.sqrt(np.mean(ref["o"] ** 2)))
+            dw_ref = expected_dw(ref, before[k], dw_gpu, w.lr, inp["scales"][k], wd, cautious,
+                                 margin=8 * t * rms)
+            err = oracle.relative_frobenius_error(dw_gpu, dw_ref)
+            assert err <= t, (step, shape, err)
+            assert oracle.relative_frobenius_error(to64(inp["bufs"][k]), ref["buf"]) <= BUF_TOL
+            if normuon:
+                v_err = oracle.relative_frobenius_error(to64(vs[k]), ref["v"])
+                assert v_err <= 2 * t, (step, shape, v_err)
+                st["v"] = to64(vs[k])  # carry the GPU's state, as the caller would
+            st["buf"] = to64(inp["bufs"][k])
+
+
+@pytest.mark.parametrize("compute", ["bf16", "fp32"])
+@pytest.mark.parametrize("cautious", [True, False])
+def test_weight_decay(compute, cautious):
+    run_case(compute, wd=0.5, cautious=cautious, normuon=False)
+
+
+@pytest.mark.parametrize("compute", ["bf16", "fp32"])
+def test_normuon(compute):
+    run_case(compute, wd=0.0, cautious=True, normuon=True)
+
+
+@pytest.mark.parametrize("compute", ["bf16", "fp32"])
+def test_normuon_with_cautious_decay_two_steps(compute):
+    run_case(compute, wd=0.5, cautious=True, normuon=True, steps=2, beta2=0.75)
+
+
+def test_normuon_beta2_one_keeps_state_and_zero_eps():
+    # beta2 = 1: v stays as given; the update is O / sqrt(v) row by row
+    run_case("fp32", wd=0.0, cautious=True, normuon=True, beta2=1.0, normuon_eps=0.0,
+             shapes=((64, 192), (192, 64)))
+
+
+def test_step_ex_without_options_is_the_plain_step():
+    announce("step_ex equals step")
+    w = dataclasses.replace(wl.GPT_D768, shapes=((100, 300), (300, 100)))
+    a = wl.make_inputs(w, device=DEV)
+    b = wl.make_inputs(w, device=DEV)
+    mn.step(a["params"], a["grads"], a["bufs"], mu=w.mu, lr=w.lr, scales=a["scales"],
+            coeffs=w.coeff_table)
+    mn.step_ex(b["params"], b["grads"], b["bufs"], mu=w.mu, lr=w.lr, scales=b["scales"],
+               coeffs=w.coeff_table, weight_decay=0.0)
+    torch.cuda.synchronize()
+    for x, y in zip(a["params"] + a["bufs"], b["params"] + b["bufs"]):
+        assert torch.equal(x, y)

@@ -128,7 +128,7 @@ WORKLOADS = {w.name: w for w in
              (SINGLE_256x128, GPT_D768, GPT_D1280, GPT_3P8B, STRESS_4096x16384)}
 
 # Stream ids for the per-matrix generators.
-_GRAD, _BUF, _W, _AUX = 0, 1, 2, 3
+_GRAD, _BUF, _W, _AUX, _V = 0, 1, 2, 3, 4
 
 
 def _gen(device, seed: int, index: int, stream: int) -> torch.Generator:
@@ -210,6 +210,17 @@ def make_inputs(w: Workload, device="cpu", indices=None):
         out["params"].append(make_weight(w, i, device))
         out["scales"].append(w.scale(r, c))
     return out
+
+
+def make_second_moment(w: Workload, index: int, device="cpu") -> torch.Tensor:
+    """A seeded NorMuon second-moment state for matrix ``index``:
+    min(rows, cols) fp32 values, uniform in [0, 2/max(rows, cols)] (around
+    the mean square 1/max(rows, cols) of an orthonormal-row update), so that
+    one step already exercises the moving average."""
+    rows, cols = w.shapes[index]
+    g = _gen(device, w.seed, index, _V)
+    u = torch.rand((min(rows, cols),), generator=g, device=device, dtype=torch.float32)
+    return u * (2.0 / max(rows, cols))
 
 
 def sample_indices(w: Workload, per_group: int):
