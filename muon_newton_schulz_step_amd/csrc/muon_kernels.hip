@@ -21,6 +21,7 @@
 #include <stdint.h>
 
 #include <cstdlib>
+#include <cstring>
 #include <utility>
 
 #include "muon_kernels.h"
@@ -353,12 +354,12 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const void* p) {
 //
 // Main loop (S):
 //   S == 0  global -> registers -> LDS, two stages, the next k-tile's loads in
-//           flight while the current one is multiplied;
-//   S == 2  global -> LDS directly (global_load_lds_dwordx4), two stages, an
-//           explicit vmcnt wait and a fence-free barrier per k-tile; EARLY
-//           moves the hand-over one k-substep before the k-tile's end.
-// SCHED pins the order of MFMAs and operand reads: each later k-substep's
-// reads go one after each MFMA of the substep before it.
+//           flight while the current one is multiplied (128x128 tiles);
+//   S == 2  global -> LDS directly, two stages, an explicit vmcnt wait and a
+//           fence-free barrier per k-tile, one k-substep before the k-tile's
+//           end; the order of MFMAs and operand reads is pinned (each later
+//           k-substep's reads go one after each MFMA of the substep before).
+//           BUFLD: buffer (MUBUF) loads, else global (FLAT) ones.
 //
 // Epilogue, one 32-row block of the wave tile at a time: inputs loaded first,
 // then values computed and stored.  The accumulators hold, per lane, 4
@@ -366,10 +367,10 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const void* p) {
 // directly (consecutive lanes -> consecutive j); transposed outputs (the
 // mirrored triangle of A and B, the fp32 path's X^T) are staged in LDS as
 // [j][i] rows and stored as coalesced 16-byte chunks.
-template <typename T, int EPI, int BM, int BN, int WGM, int WGN, int S, bool SCHED, bool EARLY,
-          bool QROW, bool SPREAD = false, bool BUFLD = false>
+template <typename T, int EPI, int BM, int BN, int WGM, int WGN, int S, bool QROW, bool BUFLD>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch) {
   const GemmArgs& a = launch.a;
+  constexpr bool SCHED = S == 2;
   constexpr int NT = 64 * WGM * WGN, NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -501,12 +502,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
   // MFMA followed by one read of the next substep's operands.
   constexpr int NREAD = FM + (QROW ? 2 * FN : FN);
   constexpr int NPAIR = NREAD < FM * FN ? NREAD : FM * FN;
-  // (vmem: loads issued first in each substep, a std::integral_constant)
-  auto schedule_substeps = [&](int n, auto vmem) {
+  auto schedule_substeps = [&](int n) {
     if constexpr (SCHED) {
       for (int kk = 0; kk < n; ++kk) {
-        if constexpr (decltype(vmem)::value > 0)
-          __builtin_amdgcn_sched_group_barrier(0x020, decltype(vmem)::value, 0);
 #pragma unroll
         for (int x = 0; x < NPAIR; ++x) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
@@ -528,7 +526,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
     }
     if constexpr (SCHED) {
       __builtin_amdgcn_sched_group_barrier(0x100, NREAD, 0);
-      schedule_substeps(KK - 1, std::integral_constant<int, 0>{});
+      schedule_substeps(KK - 1);
       __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
     }
   };
@@ -589,80 +587,48 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
       for (int d = 0; d < DPW; ++d) voff[d] = (unsigned)((src[d] - wbase) * (long long)sizeof(T));
     }
     // loads d0 .. d1 - 1 of k-tile kt into stage St
-    auto issue_range = [&](int kt, u32x4_t* St, int d0, int d1) {
+    auto issue = [&](int kt, u32x4_t* St) {
       const long long off = kt * kstep;
       if constexpr (BUFLD) {
         const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(wbase + off);
 #pragma unroll
-        for (int d = d0; d < d1; ++d) buffer_load_lds16(rs, voff[d], St + (wave_s * DPW + d) * 64);
+        for (int d = 0; d < DPW; ++d) buffer_load_lds16(rs, voff[d], St + (wave_s * DPW + d) * 64);
       } else {
 #pragma unroll
-        for (int d = d0; d < d1; ++d) load_lds16(src[d] + off, St + (wave_s * DPW + d) * 64);
+        for (int d = 0; d < DPW; ++d) load_lds16(src[d] + off, St + (wave_s * DPW + d) * 64);
       }
     };
-    auto issue = [&](int kt, u32x4_t* St) { issue_range(kt, St, 0, DPW); };
-    if constexpr (!EARLY) {
-      auto ktile = [&](int kt, const u32x4_t* cur, u32x4_t* nxt) {
-        wait_vmcnt<0>();     // this wave's part of k-tile kt has landed
-        barrier_no_fence();  // everyone's has; everyone is done reading nxt
-        if (kt + 1 < nk) issue(kt + 1, nxt);
-        compute(cur);
-      };
-      issue(0, S0);
-      for (int kt = 0; kt < nk; kt += 2) {
-        ktile(kt, S0, S1);
-        ktile(kt + 1, S1, S0);
-      }
-      __syncthreads();
-    } else {
-      // The waves meet once the last k-substep's operands are in registers;
-      // the k-tile after next then goes into the stage just finished, and the
-      // next k-tile's first operands are read while the last substep's MFMAs
-      // run.  No branch in the body: the final two k-tiles reload the last
-      // k-tile into a stage nobody reads any more (drained below).
-      // SPREAD: a k-tile's loads go out in LG groups, the first right after
-      // the barrier that frees its stage, the others one per k-substep of
-      // the following k-tile, so that the waves never queue all their loads
-      // at the address unit at once (a wave waiting to issue a load cannot
-      // issue its MFMAs either).
-      constexpr int LG = SPREAD ? KK : 1;
-      constexpr int GPW = DPW / LG;  // loads per group
-      static_assert(GPW * LG == DPW, "load groups");
-      auto issue_group = [&](int kt, u32x4_t* St, int g) {
-        issue_range(kt, St, g * GPW, (g + 1) * GPW);
-      };
-      auto ktile = [&](int kt, u32x4_t* cur, u32x4_t* nxt) {
-        // the k-tile whose first load group went into nxt at the last barrier
-        const int kl = kt + 1 < nk ? kt + 1 : nk - 1;
+    // The waves meet once the last k-substep's operands are in registers;
+    // the k-tile after next then goes into the stage just finished, and the
+    // next k-tile's first operands are read while the last substep's MFMAs
+    // run.  No branch in the body: the final two k-tiles reload the last
+    // k-tile into a stage nobody reads any more (drained below).
+    auto ktile = [&](int kt, u32x4_t* cur, const u32x4_t* nxt) {
 #pragma unroll
-        for (int kk = 0; kk + 1 < KK; ++kk) {
-          if (kk + 1 < LG) issue_group(kl, nxt, kk + 1);
-          fload(cur, kk + 1, (kk + 1) & 1);
-          mfmas(kk & 1);
-        }
-        schedule_substeps(KK - 1, std::integral_constant<int, (LG > 1 ? GPW : 0)>{});
-        wait_vmcnt<0>();     // this wave's part of k-tile kt+1 has landed
-        barrier_no_fence();  // everyone's has; everyone is done reading cur
-        issue_group(kt + 2 < nk ? kt + 2 : nk - 1, cur, 0);
-        fload(nxt, 0, 0);
-        mfmas((KK - 1) & 1);
-        if constexpr (SCHED) {
-          __builtin_amdgcn_sched_group_barrier(0x020, GPW, 0);  // the loads
-          schedule_substeps(1, std::integral_constant<int, 0>{});
-        }
-      };
-      issue(0, S0);
-      wait_vmcnt<0>();
-      barrier_no_fence();
-      issue_group(nk > 1 ? 1 : 0, S1, 0);
-      fload(S0, 0, 0);
-      for (int kt = 0; kt < nk; kt += 2) {
-        ktile(kt, S0, S1);
-        ktile(kt + 1, S1, S0);
+      for (int kk = 0; kk + 1 < KK; ++kk) {
+        fload(cur, kk + 1, (kk + 1) & 1);
+        mfmas(kk & 1);
       }
-      wait_vmcnt<0>();
-      __syncthreads();
+      schedule_substeps(KK - 1);
+      wait_vmcnt<0>();     // this wave's part of k-tile kt+1 has landed
+      barrier_no_fence();  // everyone's has; everyone is done reading cur
+      issue(kt + 2 < nk ? kt + 2 : nk - 1, cur);
+      fload(nxt, 0, 0);
+      mfmas((KK - 1) & 1);
+      __builtin_amdgcn_sched_group_barrier(0x020, DPW, 0);  // the loads
+      schedule_substeps(1);
+    };
+    issue(0, S0);
+    wait_vmcnt<0>();
+    barrier_no_fence();
+    issue(nk > 1 ? 1 : 0, S1);
+    fload(S0, 0, 0);
+    for (int kt = 0; kt < nk; kt += 2) {
+      ktile(kt, S0, S1);
+      ktile(kt + 1, S1, S0);
     }
+    wait_vmcnt<0>();
+    __syncthreads();
   }
 
   // ---- epilogue (LDS is free: the main loop ended with a barrier)
@@ -1101,80 +1067,44 @@ int gemm_tile(int compute_bf16, int tile_pref) {
   return tile_pref == 128 ? 128 : 256;
 }
 
-// bf16 256x256 tiles on 8 waves (2x4, 128x64 each).  Main loop, chosen by
-// MUON_WAVE_CFG (a tuning knob; by default 9, and 5 for the FINALs, whose
-// epilogue-heavy tiles measured slower with buffer loads):
-//   0  register-staged loads, two LDS stages
-//   4  direct-to-LDS loads, two stages, order pinned
-//   5  as 4 with the stage hand-over one k-substep before the tile's end
-//   6, 7  as 4, 5 on 4 waves (2x2, 128x128 each, accumulators in AGPRs)
-//   8  as 5 with each k-tile's loads spread over the next k-tile's substeps
-//   9, 10  as 5, 8 with buffer (MUBUF) instead of global direct-to-LDS loads
-// 128x128 tiles use 4 waves (64x64 each) and register-staged loads.  The
-// bf16 UPDATE / FINAL read X's hi plane as a row-major second operand.
-static int wave_cfg(int epi) {
+// bf16 256x256 tiles on 8 waves (2x4, 128x64 each) with the direct-to-LDS
+// main loop; buffer loads except for the FINALs, whose epilogue-heavy tiles
+// measured faster with global ones (MUON_LOADS=global|buffer overrides, a
+// tuning knob).  128x128 tiles use 4 waves (64x64 each) and register-staged
+// loads.  The bf16 UPDATE / FINAL read X's hi plane as a row-major second
+// operand.
+static bool buffer_loads(int epi) {
   static const int v = [] {
-    const char* e = std::getenv("MUON_WAVE_CFG");
-    return e ? std::atoi(e) : -1;
+    const char* e = std::getenv("MUON_LOADS");
+    if (!e) return -1;
+    return std::strcmp(e, "buffer") == 0 ? 1 : std::strcmp(e, "global") == 0 ? 0 : -1;
   }();
-  if (v >= 0) return v;
-  const bool final = epi == EPI_FINAL_W || epi == EPI_FINAL_OUT || epi == EPI_FINAL_W_T ||
-                     epi == EPI_FINAL_OUT_T;
-  return final ? 5 : 9;
+  if (v >= 0) return v == 1;
+  return !(epi == EPI_FINAL_W || epi == EPI_FINAL_OUT || epi == EPI_FINAL_W_T ||
+           epi == EPI_FINAL_OUT_T);
 }
 
 template <typename T, int E>
 static void launch_gemm_t(int tile, const GemmArgs& a, const WeightTable& t, dim3 grid,
                           hipStream_t s) {
   const GemmLaunch launch{a, t};
-  constexpr bool QR =
-      sizeof(T) == 2 && E != EPI_GRAM && E != EPI_POLY;
+  constexpr bool QR = sizeof(T) == 2 && E != EPI_GRAM && E != EPI_POLY;
   if constexpr (sizeof(T) == 2) {
     if (tile == 256) {
-      int cfg = wave_cfg(E);
       // buffer loads address an operand panel with 32-bit lane offsets:
       // up to 256 rows of the leading dimension
       const long long ld = a.ldp > a.ldq ? a.ldp : a.ldq;
-      if ((cfg == 9 || cfg == 10) && 256LL * ld * (long long)sizeof(T) >= (1LL << 31))
-        cfg = cfg == 9 ? 5 : 8;
-      switch (cfg) {
-        case 0:
-          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 0, false, false, QR>), grid,
-                             dim3(512), 0, s, launch);
-          return;
-        case 5:
-          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 2, true, true, QR>), grid,
-                             dim3(512), 0, s, launch);
-          return;
-        case 6:
-          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 2, 2, true, false, QR>), grid,
-                             dim3(256), 0, s, launch);
-          return;
-        case 7:
-          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 2, 2, true, true, QR>), grid,
-                             dim3(256), 0, s, launch);
-          return;
-        case 8:
-          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 2, true, true, QR, true>), grid,
-                             dim3(512), 0, s, launch);
-          return;
-        case 9:
-          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 2, true, true, QR, false, true>),
-                             grid, dim3(512), 0, s, launch);
-          return;
-        case 10:
-          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 2, true, true, QR, true, true>),
-                             grid, dim3(512), 0, s, launch);
-          return;
-        default:
-          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 2, true, false, QR>), grid,
-                             dim3(512), 0, s, launch);
-          return;
-      }
+      if (buffer_loads(E) && 256LL * ld * (long long)sizeof(T) < (1LL << 31))
+        hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 2, QR, true>), grid, dim3(512), 0,
+                           s, launch);
+      else
+        hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 2, QR, false>), grid, dim3(512), 0,
+                           s, launch);
+      return;
     }
   }
-  hipLaunchKernelGGL((gemm_kernel<T, E, 128, 128, 2, 2, 0, false, false, QR>), grid, dim3(256),
-                     0, s, launch);
+  hipLaunchKernelGGL((gemm_kernel<T, E, 128, 128, 2, 2, 0, QR, false>), grid, dim3(256), 0, s,
+                     launch);
 }
 
 hipError_t launch_gemm(int compute_bf16, int epi, int tile, const GemmArgs& a_in,
