@@ -790,6 +790,82 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
     }
   }
 
+  // UPDATE on the bf16 path: X's hi and lo planes move in runs of 8
+  // consecutive columns (16-byte accesses, 8 lanes per 128-byte row segment)
+  // instead of one 2-byte element per lane and access.  Each wave writes its
+  // accumulators of one 32-row block as fp32 rows into its own LDS area and
+  // reads them back as runs; the next block's hi and lo are loaded while this
+  // one is staged.  Only the wave itself touches its area and a wave's LDS
+  // accesses execute in issue order, so a compiler barrier orders them.
+  if constexpr (EPI == EPI_UPDATE && HILO) {
+    constexpr int RPL = WTN / 8;         // runs per staged row
+    constexpr int RSTEP = 64 / RPL;      // rows between a lane's runs
+    constexpr int RUNS = 32 / RSTEP;     // runs per lane and block
+    static_assert(WTN == 64 && RUNS * RSTEP == 32, "64-column wave tiles");
+    static_assert(QROW && (size_t)NW * 32 * WTN * 4 <= (size_t)STAGE * 16,
+                  "the staged blocks fit in one stage");
+    float* __restrict__ Tw = reinterpret_cast<float*>(S0) + wave * 32 * WTN;
+    // 16-byte unit u of staged row r sits at unit u ^ (r & 1) ^ 8 ((r >> 2) & 1):
+    // the accumulator writes (rows r and r + 4 in the two half-waves) and the
+    // run reads (two rows per 16 lanes) are free of bank conflicts
+    auto slot = [](int r, int c) __attribute__((always_inline)) {
+      return r * WTN + ((((c >> 2) ^ (r & 1) ^ (((r >> 2) & 1) << 3))) << 2) + (c & 3);
+    };
+    const int rr0 = lane / RPL, cc = 8 * (lane % RPL);  // run s: row rr0 + RSTEP s
+    auto offset = [&](int mi, int s) __attribute__((always_inline)) {
+      return (long long)(i_base + mi * 32 + rr0 + RSTEP * s) * a.ldx + j_base + cc;
+    };
+    u32x4_t hv[2][RUNS], lv[2][RUNS];
+    auto load = [&](auto mi, auto b) __attribute__((always_inline)) {
+      static_for<RUNS>([&](auto s) {
+        const long long o = offset(decltype(mi)::value, s);
+        hv[decltype(b)::value][s] = *reinterpret_cast<const u32x4_t*>(Xh + o);
+        lv[decltype(b)::value][s] = *reinterpret_cast<const u32x4_t*>(Xl + o);
+      });
+    };
+    load(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+    static_for<FM>([&](auto mi) {
+      constexpr int b = decltype(mi)::value & 1;
+      if constexpr (decltype(mi)::value + 1 < FM)
+        load(std::integral_constant<int, decltype(mi)::value + 1>{},
+             std::integral_constant<int, b ^ 1>{});
+      static_for<FN>([&](auto ni) {
+        static_for<16>([&](auto r) {
+          Tw[slot(8 * (r / 4) + 4 * hsel + r % 4, 32 * ni + (lane & 31))] = acc[mi][ni][(int)r];
+        });
+      });
+      asm volatile("" ::: "memory");
+      static_for<RUNS>([&](auto s) {
+        const int r = rr0 + RSTEP * s;
+        const f32x4_t p0 = *reinterpret_cast<const f32x4_t*>(Tw + slot(r, cc));
+        const f32x4_t p1 = *reinterpret_cast<const f32x4_t*>(Tw + slot(r, cc + 4));
+        u32x4_t ho, lo;
+        static_for<4>([&](auto w) {
+          const unsigned hw = hv[b][s][(int)w], lw = lv[b][s][(int)w];
+          unsigned short hb[2], lb[2];
+          static_for<2>([&](auto h) {
+            constexpr int e = 2 * w + h;
+            const float x = __uint_as_float(h ? hw & 0xffff0000u : hw << 16) +
+                            __uint_as_float(h ? lw & 0xffff0000u : lw << 16);
+            const float accv = e < 4 ? p0[e & 3] : p1[e & 3];
+            bf16_t vh, vl;
+            split_bf16(scl * (a.a * x + accv), vh, vl);
+            hb[h] = __builtin_bit_cast(unsigned short, vh);
+            lb[h] = __builtin_bit_cast(unsigned short, vl);
+          });
+          ho[(int)w] = (unsigned)hb[0] | ((unsigned)hb[1] << 16);
+          lo[(int)w] = (unsigned)lb[0] | ((unsigned)lb[1] << 16);
+        });
+        const long long o = offset(mi, s);
+        // lo is updated in place: only this block reads X[i][j]'s lo
+        *reinterpret_cast<u32x4_t*>(Xh_next + o) = ho;
+        *reinterpret_cast<u32x4_t*>(Xl + o) = lo;
+      });
+      asm volatile("" ::: "memory");  // this block's reads before the next one's writes
+    });
+    return;
+  }
+
   // Epilogue passes: EPN accumulator column blocks and EPQ of the 4 row
   // quads of one 32-row block at a time (FINAL_W has a third input, so its
   // passes are smaller to keep the loads in flight within the registers).
