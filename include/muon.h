@@ -122,7 +122,8 @@ int muon_orthogonalize(const void* in, int in_dtype, void* out, int out_dtype,
  *   scale          host array of n per-matrix multipliers of lr.
  *   coeffs, n_steps, eps, compute, workspace: as for muon_orthogonalize,
  *                  with the workspace from muon_step_workspace_bytes.
- * params[i], grads[i] and momentum[i] must not overlap one another.
+ * params[i], grads[i] and momentum[i] must not overlap one another or the
+ * workspace (MUON_ERR_INVALID_ARG).
  * n == 0 returns MUON_OK with nothing enqueued. */
 int muon_step(int n, const int* rows, const int* cols,
               void* const* params, int param_dtype,
@@ -164,7 +165,7 @@ size_t muon_step_ex_workspace_bytes(int n, const int* rows, const int* cols, int
  *                  elements each, in/out (read and written only when
  *                  options->normuon; may be NULL otherwise).  Each is
  *                  4-byte aligned and overlaps none of params[i], grads[i],
- *                  momentum[i].
+ *                  momentum[i] and the workspace.
  *   options        NULL: exactly muon_step.
  * For each matrix i: momentum and orthogonalisation as in muon_step, then
  * (normuon) O' and v' as above, then the decayed weight update with O'.

@@ -134,7 +134,11 @@ hipError_t timed(int kind, int m, int n, int batch, int step, double flops, doub
   hipError_t err = hipEventCreate(&e0);
   if (err == hipSuccess) err = hipEventCreate(&e1);
   if (err == hipSuccess) err = hipEventRecord(e0, s);
-  if (err != hipSuccess) return err;
+  if (err != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    return err;
+  }
   err = launch();
   const hipError_t err2 = hipEventRecord(e1, s);
   if (err == hipSuccess) err = err2;
@@ -410,6 +414,15 @@ int step_impl(int n, const int* rows, const int* cols, void* const* params, int 
   if (need == 0) return MUON_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < need || !aligned(workspace, kWsAlign))
     return MUON_ERR_WORKSPACE;
+  for (int i = 0; i < n; ++i) {
+    const size_t el = (size_t)rows[i] * cols[i];
+    if (overlap(workspace, need, params[i], el * 4) ||
+        overlap(workspace, need, grads[i], el * gsz) ||
+        overlap(workspace, need, momentum[i], el * 4) ||
+        (normuon && overlap(workspace, need, second_moment[i],
+                            (size_t)(rows[i] < cols[i] ? rows[i] : cols[i]) * 4)))
+      return MUON_ERR_INVALID_ARG;
+  }
 
   const bool cbf16 = compute == MUON_BF16;
   std::vector<Group> groups;

@@ -113,6 +113,9 @@ def step_call(n=2, rows=(8, 16), cols=(16, 8), params=None, grads=None, bufs=Non
     (dict(n_steps=65, coeffs=Q * 13), mn.MUON_ERR_INVALID_ARG),
     (dict(ws=0), mn.MUON_ERR_WORKSPACE),
     (dict(ws_bytes=100), mn.MUON_ERR_WORKSPACE),
+    (dict(ws=FAKE * 64), mn.MUON_ERR_INVALID_ARG),           # workspace overlaps a weight
+    (dict(ws=FAKE * 128 + 4096), mn.MUON_ERR_INVALID_ARG),   # ... a gradient
+    (dict(ws=FAKE * 64 + 8192 - 256), mn.MUON_ERR_INVALID_ARG),  # ... a momentum buffer
 ])
 def test_step_rejects_before_enqueue(kw, expect):
     assert step_call(**kw) == expect
@@ -157,6 +160,7 @@ OPT = dict(weight_decay=0.1, cautious=1, normuon=1, beta2=0.95, normuon_eps=1e-8
     (dict(vs=[FAKE * 64 + 16386, FAKE * 128 + 16384]), mn.MUON_ERR_INVALID_ARG),  # misaligned
     (dict(vs=[FAKE * 64 + 8, FAKE * 128 + 16384]), mn.MUON_ERR_INVALID_ARG),      # overlaps W
     (dict(ws=0), mn.MUON_ERR_WORKSPACE),
+    (dict(vs=[FAKE * 4096 + 256, FAKE * 128 + 16384]), mn.MUON_ERR_INVALID_ARG),  # in workspace
 ])
 def test_step_ex_rejects_before_enqueue(kw, expect):
     assert step_ex_call(**kw) == expect
