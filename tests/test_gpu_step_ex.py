@@ -112,3 +112,34 @@ def test_step_ex_without_options_is_the_plain_step():
     torch.cuda.synchronize()
     for x, y in zip(a["params"] + a["bufs"], b["params"] + b["bufs"]):
         assert torch.equal(x, y)
+
+
+def test_gpt_3p8b_step_ex_sampled():
+    # the full 168-matrix 3.8B set through muon_step_ex with NorMuon and
+    # cautious decay (the bench's normuon_cwd variant); the oracle checks one
+    # matrix of every raw shape, weights and second moments
+    announce("gpt 3.8b all 168, step_ex normuon + cautious decay, oracle on samples")
+    w = wl.GPT_3P8B
+    inp = wl.make_inputs(w, device=DEV)
+    vs = [wl.make_second_moment(w, i, device=DEV) for i in range(len(w.shapes))]
+    samples = wl.sample_indices(w, 1) + [len(w.shapes) - 1]
+    before = {k: to64(inp["params"][k]) for k in samples}
+    bufs = {k: to64(inp["bufs"][k]) for k in samples}
+    v0 = {k: to64(vs[k]) for k in samples}
+    opt = dict(weight_decay=0.1, cautious=True, beta2=0.95, normuon_eps=1e-8)
+    mn.step_ex(inp["params"], inp["grads"], inp["bufs"], mu=w.mu, lr=w.lr,
+               scales=inp["scales"], coeffs=w.coeff_table, compute="bf16",
+               second_moments=vs, **opt)
+    torch.cuda.synchronize()
+    for k in samples:
+        print("  oracle matrix", k, w.shapes[k], flush=True)
+        ref = oracle.muon_step_ex(before[k], to64(inp["grads"][k]), bufs[k], w.mu, w.lr,
+                                  inp["scales"][k], w.coeff_table, second_moment=v0[k], **opt)
+        t = tol("bf16", w.shapes[k])
+        dw_gpu = to64(inp["params"][k]) - before[k]
+        rms = float(np.sqrt(np.mean(ref["o"] ** 2)))
+        dw_ref = expected_dw(ref, before[k], dw_gpu, w.lr, inp["scales"][k], 0.1, True,
+                             margin=8 * t * rms)
+        assert oracle.relative_frobenius_error(dw_gpu, dw_ref) <= t, k
+        assert oracle.relative_frobenius_error(to64(inp["bufs"][k]), ref["buf"]) <= BUF_TOL
+        assert oracle.relative_frobenius_error(to64(vs[k]), ref["v"]) <= 2 * t
