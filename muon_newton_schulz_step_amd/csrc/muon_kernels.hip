@@ -354,7 +354,7 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const void* p) {
 //
 // Main loop (S):
 //   S == 0  global -> registers -> LDS, two stages, the next k-tile's loads in
-//           flight while the current one is multiplied (128x128 tiles);
+//           flight while the current one is multiplied (the fp32 path);
 //   S == 2  global -> LDS directly, two stages, an explicit vmcnt wait and a
 //           fence-free barrier per k-tile, one k-substep before the k-tile's
 //           end; the order of MFMAs and operand reads is pinned (each later
@@ -1143,12 +1143,12 @@ int gemm_tile(int compute_bf16, int tile_pref) {
   return tile_pref == 128 ? 128 : 256;
 }
 
-// bf16 256x256 tiles on 8 waves (2x4, 128x64 each) with the direct-to-LDS
-// main loop; buffer loads except for the FINALs, whose epilogue-heavy tiles
-// measured faster with global ones (MUON_LOADS=global|buffer overrides, a
-// tuning knob).  128x128 tiles use 4 waves (64x64 each) and register-staged
-// loads.  The bf16 UPDATE / FINAL read X's hi plane as a row-major second
-// operand.
+// bf16: 256x256 tiles on 8 waves (2x4, 128x64 each) or 128x128 tiles on 4
+// waves (2x2, 64x64 each), both with the direct-to-LDS main loop; buffer
+// loads except for the FINALs, whose epilogue-heavy tiles measured faster
+// with global ones (MUON_LOADS=global|buffer overrides, a tuning knob).  The
+// bf16 UPDATE / FINAL read X's hi plane as a row-major second operand.
+// fp32: 128x128 tiles on 4 waves with register-staged loads.
 static bool buffer_loads(int epi) {
   static const int v = [] {
     const char* e = std::getenv("MUON_LOADS");
@@ -1166,18 +1166,26 @@ static void launch_gemm_t(int tile, const GemmArgs& a, const WeightTable& t, dim
   const GemmLaunch launch{a, t};
   constexpr bool QR = sizeof(T) == 2 && E != EPI_GRAM && E != EPI_POLY;
   if constexpr (sizeof(T) == 2) {
+    // buffer loads address an operand panel with 32-bit lane offsets: up to
+    // `tile` rows of the leading dimension
+    const long long ld = a.ldp > a.ldq ? a.ldp : a.ldq;
+    const bool buf = buffer_loads(E) && (long long)tile * ld * (long long)sizeof(T) < (1LL << 31);
     if (tile == 256) {
-      // buffer loads address an operand panel with 32-bit lane offsets:
-      // up to 256 rows of the leading dimension
-      const long long ld = a.ldp > a.ldq ? a.ldp : a.ldq;
-      if (buffer_loads(E) && 256LL * ld * (long long)sizeof(T) < (1LL << 31))
+      if (buf)
         hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 2, QR, true>), grid, dim3(512), 0,
                            s, launch);
       else
         hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 2, QR, false>), grid, dim3(512), 0,
                            s, launch);
-      return;
+    } else {
+      if (buf)
+        hipLaunchKernelGGL((gemm_kernel<T, E, 128, 128, 2, 2, 2, QR, true>), grid, dim3(256), 0,
+                           s, launch);
+      else
+        hipLaunchKernelGGL((gemm_kernel<T, E, 128, 128, 2, 2, 2, QR, false>), grid, dim3(256), 0,
+                           s, launch);
     }
+    return;
   }
   hipLaunchKernelGGL((gemm_kernel<T, E, 128, 128, 2, 2, 0, QR, false>), grid, dim3(256), 0, s,
                      launch);
