@@ -7,11 +7,14 @@ fraction of the dense bf16 MFMA peak / roofline of the dominant kernel /
 the fp64 oracle timed on the host cores as a CPU baseline.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--compute bf16|fp32]
-                    [--variant plain|cwd|normuon_cwd]
+                    [--variant plain|cwd|normuon_cwd] [--graph]
 
 --variant times muon_step_ex instead: page 1's cautious weight decay (cwd,
 decay 0.1) or NorMuon (beta2 0.95, eps 1e-8) with it (normuon_cwd).  The
-default, plain, is the benchmark's Muon step.
+default, plain, is the benchmark's Muon step.  --graph times replays of one
+captured step instead of eager calls (the small workloads are bound by the
+host cost of their launches); the per-kernel figures then come from an eager
+pass after the timed replays.
 """
 import argparse
 import gc
@@ -43,6 +46,9 @@ def parse():
     p.add_argument("--compute", default="bf16", choices=["bf16", "fp32"])
     p.add_argument("--variant", default="plain", choices=list(VARIANTS))
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--graph", action="store_true",
+                   help="time replays of one captured step (a HIP graph: no per-launch host "
+                        "cost); the per-kernel times then come from an eager pass after it")
     p.add_argument("--cpu-sample-seconds", type=float, default=12.0,
                    help="seconds of oracle work for the CPU baseline sample")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -268,10 +274,25 @@ def main():
     torch.cuda.synchronize()
     gc.collect()
     gc.disable()
-    mn.timing_enable(True)
-    mn.timing_read()  # drop warm-up records
     stream = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    graph_ms = None
+    if args.graph:
+        # the workspace was allocated by the warm-up steps: capture allocates nothing
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            one_step()
+        graph.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = e0.elapsed_time(e1) / args.steps
+        del graph
+    mn.timing_enable(True)
+    mn.timing_read()  # drop warm-up records
     torch.cuda.synchronize()
     e0.record(stream)
     for _ in range(args.steps):
@@ -280,7 +301,7 @@ def main():
     torch.cuda.synchronize()
     mn.timing_enable(False)
     gc.enable()
-    ms_per_step = e0.elapsed_time(e1) / args.steps
+    ms_per_step = graph_ms if args.graph else e0.elapsed_time(e1) / args.steps
     records = mn.timing_read()
     kernels = kernel_summary(records, args.steps)
     ns = [k for k in kernels if k["kind"] in ("gram", "poly", "update", "final")]
@@ -325,6 +346,7 @@ def main():
                    **({"options": opt} if opt else {}),
                    "oriented_groups": {f"{m}x{n}": c for (m, n), c in groups.items()},
                    "ns_steps": w.n_steps, "coeffs": list(w.coeffs),
+                   "launch": "hip graph replay" if args.graph else "eager",
                    "parallelism": "single GPU (one GPU's share of a matrix-sharded step)"},
         "ns_tflops": round(ns_tflops, 2),
         "ns_ms_per_step": round(ns_ms, 3),
