@@ -14,7 +14,11 @@
 //                    UPDATE X <- a X + B X   (bf16: Q is X's hi plane, read
 //                                             row-major and transposed in LDS;
 //                                             fp32: Q = X^T, kept as a copy)
-//                    FINAL  the last UPDATE, into the weights or the output
+//                    FINAL  the last UPDATE, into the weights (with page 1's
+//                           decoupled or cautious weight decay) or the output
+//   normuon_rows_kernel  NorMuon (page 1): per oriented row, the mean of O^2,
+//                        the second-moment update and the row's scale
+//   apply_kernel         with NorMuon, the weight update as its own pass
 // The 1/||u|| normalisation is folded into the first GRAM (x inv^2) and
 // UPDATE (x inv) epilogues.
 #include <hip/hip_runtime.h>
@@ -363,10 +367,13 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const void* p) {
 //
 // Epilogue, one 32-row block of the wave tile at a time: inputs loaded first,
 // then values computed and stored.  The accumulators hold, per lane, 4
-// consecutive rows i of one column j, so row-major outputs are stored
-// directly (consecutive lanes -> consecutive j); transposed outputs (the
-// mirrored triangle of A and B, the fp32 path's X^T) are staged in LDS as
-// [j][i] rows and stored as coalesced 16-byte chunks.
+// consecutive rows i of one column j, so row-major outputs can be stored
+// directly (consecutive lanes -> consecutive j): GRAM, POLY and the FINAL of
+// wide matrices do so.  The bf16 UPDATE instead stages each block as fp32
+// rows in LDS and moves X in 16-byte runs of 8 columns; transposed outputs
+// (the mirrored triangle of A and B, the fp32 path's X^T, the weights of a
+// tall matrix) are staged in LDS as [j][i] rows and stored as coalesced
+// 16-byte chunks.
 template <typename T, int EPI, int BM, int BN, int WGM, int WGN, int S, bool QROW, bool BUFLD>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch) {
   const GemmArgs& a = launch.a;
