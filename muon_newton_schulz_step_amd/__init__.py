@@ -94,6 +94,17 @@ class Workspace:
 _default_ws: dict = {}
 
 
+def _check_device(device, **tensors):
+    """Every tensor must live on `device`, a GPU: the library is handed raw
+    device pointers, so host or other-device tensors are refused here."""
+    if device.type != "cuda":
+        raise ValueError("tensors must be GPU tensors")
+    for name, ts in tensors.items():
+        for t in ts:
+            if t is not None and t.device != device:
+                raise ValueError(f"{name}: every tensor must be on {device}, found {t.device}")
+
+
 def _workspace(nbytes: int, device, workspace):
     if workspace is None:
         workspace = _default_ws.setdefault(str(device), Workspace())
@@ -136,8 +147,8 @@ def orthogonalize(x, coeffs=QUINTIC, n_steps=None, *, eps=DEFAULT_EPS, compute="
     if n_steps is None and isinstance(coeffs[0], (int, float)):
         n_steps = 5
     table, n_steps = _coeffs(coeffs, n_steps)
-    if not x.is_cuda:
-        raise ValueError("x must be a GPU tensor")
+    _check_device(x.device, out=[out], workspace=[
+        workspace if workspace is not None and not isinstance(workspace, Workspace) else None])
     squeeze = x.dim() == 2
     xb = x.unsqueeze(0) if squeeze else x
     if xb.dim() != 3:
@@ -152,12 +163,13 @@ def orthogonalize(x, coeffs=QUINTIC, n_steps=None, *, eps=DEFAULT_EPS, compute="
             raise ValueError("out must be contiguous")
     c = _compute_code(compute)
     need = orthogonalize_workspace_bytes(max(batch, 1), rows, cols, compute)
-    wptr, wbytes = _workspace(need, x.device, workspace)
-    st = lib().muon_orthogonalize(
-        ctypes.c_void_p(xb.data_ptr()), _dtype_code(xb.dtype),
-        ctypes.c_void_p(out.data_ptr()), _dtype_code(out.dtype),
-        batch, rows, cols, rows * cols, table, n_steps, float(eps), c,
-        ctypes.c_void_p(wptr), wbytes, _stream(x.device))
+    with torch.cuda.device(x.device):
+        wptr, wbytes = _workspace(need, x.device, workspace)
+        st = lib().muon_orthogonalize(
+            ctypes.c_void_p(xb.data_ptr()), _dtype_code(xb.dtype),
+            ctypes.c_void_p(out.data_ptr()), _dtype_code(out.dtype),
+            batch, rows, cols, rows * cols, table, n_steps, float(eps), c,
+            ctypes.c_void_p(wptr), wbytes, _stream(x.device))
     if st != MUON_OK:
         raise MuonError(st, "muon_orthogonalize")
     return out[0] if squeeze else out
@@ -216,32 +228,37 @@ def _step(params, grads, bufs, second_moments, opt, *, mu, lr, scales, coeffs, n
             raise ValueError("tensors must be contiguous")
         if _dtype_code(g.dtype) != grad_dtype:
             raise ValueError("all grads must share one dtype")
+    device = params[0].device
+    _check_device(device, params=params, grads=grads, bufs=bufs,
+                  second_moments=second_moments or [],
+                  workspace=[workspace if workspace is not None
+                             and not isinstance(workspace, Workspace) else None])
     shapes = [tuple(p.shape) for p in params]
     rows = _lib.int_array(r for r, _ in shapes)
     cols = _lib.int_array(c for _, c in shapes)
     c = _compute_code(compute)
-    device = params[0].device
     common = (_lib.ptr_array(p.data_ptr() for p in params), _dtype_code(params[0].dtype),
               _lib.ptr_array(g.data_ptr() for g in grads), grad_dtype,
               _lib.ptr_array(b.data_ptr() for b in bufs))
-    if opt is None:
-        need = int(lib().muon_step_workspace_bytes(n, rows, cols, c))
-        wptr, wbytes = _workspace(need, device, workspace)
-        st = lib().muon_step(
-            n, rows, cols, *common,
-            float(mu), float(lr), _lib.float_array(scales), table, n_steps, float(eps), c,
-            ctypes.c_void_p(wptr), wbytes, _stream(device))
-        where = "muon_step"
-    else:
-        need = int(lib().muon_step_ex_workspace_bytes(n, rows, cols, c, ctypes.byref(opt)))
-        wptr, wbytes = _workspace(need, device, workspace)
-        vptrs = (_lib.ptr_array(v.data_ptr() for v in second_moments)
-                 if second_moments is not None else None)
-        st = lib().muon_step_ex(
-            n, rows, cols, *common, vptrs,
-            float(mu), float(lr), _lib.float_array(scales), table, n_steps, float(eps), c,
-            ctypes.byref(opt), ctypes.c_void_p(wptr), wbytes, _stream(device))
-        where = "muon_step_ex"
+    with _torch().cuda.device(device):
+        if opt is None:
+            need = int(lib().muon_step_workspace_bytes(n, rows, cols, c))
+            wptr, wbytes = _workspace(need, device, workspace)
+            st = lib().muon_step(
+                n, rows, cols, *common,
+                float(mu), float(lr), _lib.float_array(scales), table, n_steps, float(eps), c,
+                ctypes.c_void_p(wptr), wbytes, _stream(device))
+            where = "muon_step"
+        else:
+            need = int(lib().muon_step_ex_workspace_bytes(n, rows, cols, c, ctypes.byref(opt)))
+            wptr, wbytes = _workspace(need, device, workspace)
+            vptrs = (_lib.ptr_array(v.data_ptr() for v in second_moments)
+                     if second_moments is not None else None)
+            st = lib().muon_step_ex(
+                n, rows, cols, *common, vptrs,
+                float(mu), float(lr), _lib.float_array(scales), table, n_steps, float(eps), c,
+                ctypes.byref(opt), ctypes.c_void_p(wptr), wbytes, _stream(device))
+            where = "muon_step_ex"
     if st != MUON_OK:
         raise MuonError(st, where)
 

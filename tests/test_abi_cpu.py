@@ -226,3 +226,16 @@ def test_timing_log_empty_without_launches():
     prev = mn.timing_enable(True)
     assert mn.timing_read() == []
     mn.timing_enable(prev)
+
+
+def test_binding_refuses_host_tensors():
+    # the library takes raw device pointers: host tensors never reach it
+    import torch
+    p, g, b = torch.zeros(8, 16), torch.zeros(8, 16, dtype=torch.bfloat16), torch.zeros(8, 16)
+    with pytest.raises(ValueError, match="GPU"):
+        mn.step([p], [g], [b], mu=0.95, lr=0.02)
+    with pytest.raises(ValueError, match="GPU"):
+        mn.step_ex([p], [g], [b], mu=0.95, lr=0.02, weight_decay=0.1,
+                   second_moments=[torch.zeros(8)], beta2=0.95, normuon_eps=1e-8)
+    with pytest.raises(ValueError, match="GPU"):
+        mn.orthogonalize(torch.zeros(8, 16))

@@ -139,3 +139,22 @@ def test_stress_full_shape_reduced_batch():
             assert err <= tol(compute)
         del gt
         torch.cuda.empty_cache()
+
+
+def test_refuses_tensors_off_the_device():
+    # every tensor must be on the weights' GPU; a host gradient, momentum
+    # buffer or workspace is refused before anything is enqueued
+    announce("device checks")
+    p = torch.zeros(8, 16, device=DEV)
+    g = torch.zeros(8, 16, dtype=torch.bfloat16, device=DEV)
+    b = torch.zeros(8, 16, device=DEV)
+    for kw in (dict(grads=[g.cpu()]), dict(bufs=[b.cpu()]),
+               dict(workspace=torch.empty(1 << 20, dtype=torch.uint8))):
+        args = dict(params=[p], grads=[g], bufs=[b])
+        args.update({k: v for k, v in kw.items() if k != "workspace"})
+        with pytest.raises(ValueError):
+            mn.step(args["params"], args["grads"], args["bufs"], mu=0.95, lr=0.02,
+                    workspace=kw.get("workspace"))
+    with pytest.raises(ValueError):
+        mn.orthogonalize(g, out=torch.empty(8, 16))
+    assert torch.count_nonzero(p) == 0 and torch.count_nonzero(b) == 0
