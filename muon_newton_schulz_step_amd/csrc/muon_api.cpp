@@ -262,6 +262,11 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
     // tall matrices: runs of 4 elements of a stored row (length m) are
     // aligned when m and the output's matrix stride are multiples of 4
     g.vec_tall = L.m % 4 == 0 && (c.final_mode != FINAL_OUT || c.s_out % 4 == 0);
+    // wide matrices: runs of 8 elements of a stored row (length n) are
+    // 16-byte aligned when n (bf16 output: and the matrix stride) allows
+    g.vec_wide = c.final_mode == FINAL_OUT && c.out_bf16
+                     ? L.n % 8 == 0 && c.s_out % 8 == 0
+                     : L.n % 4 == 0 && (c.final_mode != FINAL_OUT || c.s_out % 4 == 0);
     g.neg_lrwd = c.neg_lrwd;
     g.cautious = c.cautious;
     // reads B and the operand X; the epilogue reads X (bf16: hi + lo, fp32:

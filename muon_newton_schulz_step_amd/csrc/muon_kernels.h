@@ -81,6 +81,8 @@ struct GemmArgs {
   void* out; long long s_out; int out_bf16;
   int vec_tall;            // FINAL of tall matrices: 4 consecutive i of a
                            // weight / output row are 16- (8-) byte aligned
+  int vec_wide;            // FINAL of wide matrices (bf16): 8 consecutive j
+                           // of a weight / output row are 16-byte aligned
   float neg_lrwd;          // FINAL_W: -lr * weight_decay (0: no decay)
   int cautious;            // FINAL_W: decay only where O * W >= 0
   float neg_lr;

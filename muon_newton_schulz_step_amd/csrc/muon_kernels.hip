@@ -797,14 +797,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
     }
   }
 
-  // UPDATE on the bf16 path: X's hi and lo planes move in runs of 8
-  // consecutive columns (16-byte accesses, 8 lanes per 128-byte row segment)
-  // instead of one 2-byte element per lane and access.  Each wave writes its
+  // UPDATE and the FINAL of wide matrices on the bf16 path: X's hi and lo
+  // planes move in runs of 8 consecutive columns (16-byte accesses, 8 lanes
+  // per 128-byte row segment) instead of one 2-byte element per lane and
+  // access, and so do the weights (or the output) where their rows are
+  // 16-byte aligned (vec_wide), element by element at ragged edges.  Each wave writes its
   // accumulators of one 32-row block as fp32 rows into its own LDS area and
   // reads them back as runs; the next block's hi and lo are loaded while this
   // one is staged.  Only the wave itself touches its area and a wave's LDS
   // accesses execute in issue order, so a compiler barrier orders them.
-  if constexpr (EPI == EPI_UPDATE && HILO) {
+  if constexpr ((EPI == EPI_UPDATE || (FINAL && !TALLF)) && HILO) {
     constexpr int RPL = WTN / 8;         // runs per staged row
     constexpr int RSTEP = 64 / RPL;      // rows between a lane's runs
     constexpr int RUNS = 32 / RSTEP;     // runs per lane and block
@@ -842,10 +844,88 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
         });
       });
       asm volatile("" ::: "memory");
+      // FINAL: this block's weights (or nothing, for the output), loaded
+      // before the block is staged
+      [[maybe_unused]] f32x4_t wv[FIN_W ? RUNS : 1][2];
+      if constexpr (FIN_W) {
+        static_for<RUNS>([&](auto s) {
+          const int i = i_base + mi * 32 + rr0 + RSTEP * s, j = j_base + cc;
+          const float* Wr = W + (long long)i * a.n + j;
+          if (i < a.m && a.vec_wide && j + 8 <= a.n) {
+            wv[s][0] = *reinterpret_cast<const f32x4_t*>(Wr);
+            wv[s][1] = *reinterpret_cast<const f32x4_t*>(Wr + 4);
+          } else {
+            static_for<8>([&](auto e) {
+              wv[s][e / 4][e % 4] = i < a.m && j + e < a.n ? Wr[(int)e] : 0.f;
+            });
+          }
+        });
+      }
       static_for<RUNS>([&](auto s) {
         const int r = rr0 + RSTEP * s;
         const f32x4_t p0 = *reinterpret_cast<const f32x4_t*>(Tw + slot(r, cc));
         const f32x4_t p1 = *reinterpret_cast<const f32x4_t*>(Tw + slot(r, cc + 4));
+        if constexpr (FINAL) {
+          float x[8];
+          static_for<4>([&](auto w) {
+            const unsigned hw = hv[b][s][(int)w], lw = lv[b][s][(int)w];
+            static_for<2>([&](auto h) {
+              constexpr int e = 2 * w + h;
+              const float xe = __uint_as_float(h ? hw & 0xffff0000u : hw << 16) +
+                               __uint_as_float(h ? lw & 0xffff0000u : lw << 16);
+              x[e] = scl * (a.a * xe + (e < 4 ? p0[e & 3] : p1[e & 3]));
+            });
+          });
+          const int i = i_base + mi * 32 + r, j = j_base + cc;
+          if (i < a.m) {
+            const bool full = a.vec_wide && j + 8 <= a.n;
+            if constexpr (FIN_W) {
+              float* Wr = W + (long long)i * a.n + j;
+              f32x4_t w0, w1;
+              static_for<4>([&](auto t) {
+                w0[(int)t] = weight_step(wv[s][0][(int)t], x[t], wscale, a.neg_lrwd, a.cautious);
+                w1[(int)t] = weight_step(wv[s][1][(int)t], x[4 + t], wscale, a.neg_lrwd, a.cautious);
+              });
+              if (full) {
+                *reinterpret_cast<f32x4_t*>(Wr) = w0;
+                *reinterpret_cast<f32x4_t*>(Wr + 4) = w1;
+              } else {
+                static_for<8>([&](auto e) {
+                  if (j + e < a.n) Wr[(int)e] = e < 4 ? w0[e & 3] : w1[e & 3];
+                });
+              }
+            } else {
+              const long long oo = (long long)mat * a.s_out + (long long)i * a.n + j;
+              if (a.out_bf16) {
+                bf16_t* ob = static_cast<bf16_t*>(a.out) + oo;
+                if (full) {
+                  u32x4_t pk;
+                  static_for<4>([&](auto w) {
+                    pk[(int)w] =
+                        (unsigned)__builtin_bit_cast(unsigned short, from_f32<bf16_t>(x[2 * w])) |
+                        ((unsigned)__builtin_bit_cast(unsigned short,
+                                                      from_f32<bf16_t>(x[2 * w + 1])) << 16);
+                  });
+                  *reinterpret_cast<u32x4_t*>(ob) = pk;
+                } else {
+                  static_for<8>([&](auto e) {
+                    if (j + e < a.n) ob[(int)e] = from_f32<bf16_t>(x[e]);
+                  });
+                }
+              } else {
+                float* of = static_cast<float*>(a.out) + oo;
+                if (full) {
+                  *reinterpret_cast<f32x4_t*>(of) = f32x4_t{x[0], x[1], x[2], x[3]};
+                  *reinterpret_cast<f32x4_t*>(of + 4) = f32x4_t{x[4], x[5], x[6], x[7]};
+                } else {
+                  static_for<8>([&](auto e) {
+                    if (j + e < a.n) of[(int)e] = x[e];
+                  });
+                }
+              }
+            }
+          }
+        } else {
         u32x4_t ho, lo;
         static_for<4>([&](auto w) {
           const unsigned hw = hv[b][s][(int)w], lw = lv[b][s][(int)w];
@@ -867,6 +947,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
         // lo is updated in place: only this block reads X[i][j]'s lo
         *reinterpret_cast<u32x4_t*>(Xh_next + o) = ho;
         *reinterpret_cast<u32x4_t*>(Xl + o) = lo;
+        }
       });
       asm volatile("" ::: "memory");  // this block's reads before the next one's writes
     });
