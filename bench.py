@@ -106,22 +106,29 @@ def traffic_from_profiles(kernel_key):
 
 
 def launch_sequence(w):
-    """(kind, m, n) of every library launch of one step, in launch order: per
-    oriented group (first appearance) and chunk of at most 64 matrices, prep,
-    norm, then gram, poly, update per Newton-Schulz step, the last update
-    being one final launch for the chunk's wide matrices and one for its tall
-    ones."""
+    """(kind, m, n) of every library launch of one bf16 step, in launch order:
+    per oriented group (first appearance) and chunk of at most 64 matrices,
+    prep, norm, then gram, poly, update per Newton-Schulz step, the last
+    update being one final launch for the chunk's wide matrices and one for
+    its tall ones.  Groups with padded N >= 4M and M >= 2048 form the Gram
+    matrix of steps 1 and 3 (not the last) in two gramq launches instead."""
+    def pad(d):
+        return (d + 255) // 256 * 256
     groups = {}
     for r, c in w.shapes:
         groups.setdefault((min(r, c), max(r, c)), []).append(r > c)
     seq = []
     for (m, n), talls in groups.items():
+        qaq = pad(n) >= 4 * pad(m) and pad(m) >= 2048
         for b0 in range(0, len(talls), 64):
             chunk = talls[b0:b0 + 64]
             finals = [("final", m, n)] * ((not all(chunk)) + any(chunk))
             seq += [("prep", m, n), ("norm", m, n)]
             for k in range(w.n_steps):
-                seq += [("gram", m, n), ("poly", m, n)]
+                if qaq and k in (1, 3) and k <= w.n_steps - 2:
+                    seq += [("gramq", m, n), ("gramq", m, n), ("poly", m, n)]
+                else:
+                    seq += [("gram", m, n), ("poly", m, n)]
                 seq += [("update", m, n)] if k < w.n_steps - 1 else finals
     return seq
 
@@ -304,14 +311,14 @@ def main():
     ms_per_step = graph_ms if args.graph else e0.elapsed_time(e1) / args.steps
     records = mn.timing_read()
     kernels = kernel_summary(records, args.steps)
-    ns = [k for k in kernels if k["kind"] in ("gram", "poly", "update", "final")]
+    ns = [k for k in kernels if k["kind"] in ("gram", "gramq", "poly", "update", "final")]
     ns_ms = sum(k["ms"] for k in ns) / args.steps
     flops = w.ns_flops_counted()
     ns_tflops = flops / (ns_ms * 1e-3) / 1e12
     step_tflops = flops / (ms_per_step * 1e-3) / 1e12
     dom = kernels[0]
     dom_key = f"{dom['kind']}_{dom['m']}x{dom['n']}"
-    bound = "mfma" if dom["kind"] in ("gram", "poly", "update", "final") else "hbm"
+    bound = "mfma" if dom["kind"] in ("gram", "gramq", "poly", "update", "final") else "hbm"
     if bound == "mfma":
         achieved = dom["flops"] / dom["launches"] / (dom["avg_launch_ms"] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK[args.compute],

@@ -97,7 +97,11 @@ int muon_plan_groups(int n, const int* rows, const int* cols, int* group_of,
  *   eps           >= 0, finite (the step's default is 1e-7).
  *   compute       MUON_BF16: bf16 MFMA operands with fp32 accumulation; X is
  *                 carried between steps as two bf16 values (hi + lo, 16
- *                 significant bits) for the a*X term; MUON_FP32: fp32 throughout.
+ *                 significant bits) for the a*X term; for matrices whose
+ *                 padded shape has n >= 4m and m >= 2048, the A of steps 1
+ *                 and 3 is formed as Q A Q from the step before (Q = aI + B;
+ *                 equal to X X^T in exact arithmetic).  MUON_FP32: fp32
+ *                 throughout, A = X X^T at every step.
  *   workspace     device, >= muon_orthogonalize_workspace_bytes(...) bytes,
  *                 MUON_WORKSPACE_ALIGN-aligned; contents on entry are ignored.
  * batch == 0 returns MUON_OK with nothing enqueued. */
@@ -192,7 +196,8 @@ typedef enum {
   MUON_K_UPDATE = 4, /* X <- a X + B X, steps before the last */
   MUON_K_FINAL = 5,  /* last step's a X + B X, written to the weights or output */
   MUON_K_NORMUON = 6, /* NorMuon row statistics and second-moment update */
-  MUON_K_APPLY = 7   /* weight update as its own pass (after NorMuon) */
+  MUON_K_APPLY = 7,  /* weight update as its own pass (after NorMuon) */
+  MUON_K_GRAMQ = 8   /* one of the two launches forming A as Q A Q, Q = aI + B */
 } muon_kernel_kind;
 
 typedef struct {

@@ -12,7 +12,8 @@ MUON_OK, MUON_ERR_INVALID_ARG, MUON_ERR_UNSUPPORTED, MUON_ERR_WORKSPACE, MUON_ER
 MUON_MAX_STEPS = 64
 MUON_WORKSPACE_ALIGN = 256
 MUON_PTR_ALIGN = 16
-KERNEL_KINDS = ("prep", "norm", "gram", "poly", "update", "final", "normuon", "apply")
+KERNEL_KINDS = ("prep", "norm", "gram", "poly", "update", "final", "normuon", "apply",
+                "gramq")
 
 # Every symbol include/muon.h declares.
 EXPORTS = (

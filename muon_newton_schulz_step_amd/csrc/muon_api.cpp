@@ -62,11 +62,26 @@ int pick_tile(bool cbf16, long long tiles_at_256, int batch) {
 //   bf16: hi plane twice (the update reads one, writes the other), lo plane;
 //   fp32: X, X^T twice (read by the update, written by it).
 // Then A and B (M x M, compute precision), the norm partials and 1/norm,
-// and with NorMuon the per-row scales 1/(sqrt(v') + eps) (M floats).
+// and with NorMuon the per-row scales 1/(sqrt(v') + eps) (M floats).  Groups
+// that form some Gram matrices as Q A Q (gram_by_qaq) add A's residual and
+// the product T (M x M bf16 each).
 struct Layout {
   int m = 0, n = 0, M = 0, N = 0, cnt = 0, nblk = 0;
-  size_t x0 = 0, x1 = 0, x2 = 0, A = 0, B = 0, part = 0, inv = 0, rinv = 0, total = 0;
+  bool qaq = false;
+  size_t x0 = 0, x1 = 0, x2 = 0, A = 0, B = 0, Alo = 0, T = 0, part = 0, inv = 0, rinv = 0,
+         total = 0;
 };
+
+// The Gram matrix of the next step is Q A Q, Q = aI + B (X' = Q X, so
+// X' X'^T = Q X X^T Q): two M x M x M products instead of one M x M x N.
+// Worth it on the bf16 path when N >= 4M, and only for large M (the two
+// launches of small matrices cost more than the one they replace).
+bool gram_by_qaq(bool cbf16, long long M, long long N) { return cbf16 && N >= 4 * M && M >= 2048; }
+
+// Steps whose Gram matrix is formed as Q A Q: 1 and 3, never the last one.
+// Steps 0 and 2 recompute it from X, so the rounding of A does not compound
+// over more than one step.
+bool qaq_step(int k, int n_steps) { return (k == 1 || k == 3) && k <= n_steps - 2; }
 
 bool make_layout(int cnt, int m, int n, bool cbf16, Layout& L, bool normuon = false) {
   const long long M = pad_dim(m), N = pad_dim(n);
@@ -86,6 +101,11 @@ bool make_layout(int cnt, int m, int n, bool cbf16, Layout& L, bool normuon = fa
   L.x2 = take((size_t)cnt * MN * es);  // bf16: lo     fp32: X^T 1
   L.A = take((size_t)cnt * MM * es);
   L.B = take((size_t)cnt * MM * es);
+  L.qaq = gram_by_qaq(cbf16, M, N);
+  if (L.qaq) {
+    L.Alo = take((size_t)cnt * MM * es);
+    L.T = take((size_t)cnt * MM * es);
+  }
   L.part = take((size_t)cnt * (size_t)L.nblk * 4);
   L.inv = take((size_t)cnt * 4);
   if (normuon) L.rinv = take((size_t)cnt * (size_t)M * 4);
@@ -179,6 +199,8 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
   void* XT[2] = {ws + L.x1, ws + L.x2};
   void* A = ws + L.A;
   void* B = ws + L.B;
+  void* Alo = ws + L.Alo;
+  void* Tq = ws + L.T;
   float* part = reinterpret_cast<float*>(ws + L.part);
   float* inv = reinterpret_cast<float*>(ws + L.inv);
   const double m = L.m, n = L.n, cnt = c.cnt;
@@ -219,17 +241,46 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
     g.inv = first ? inv : nullptr;
     g.a = coeffs[k].a; g.b = coeffs[k].b; g.c = coeffs[k].c;
     g.m = L.m; g.n = L.n; g.tall_mask = c.tall_mask;
-
-    // A = X X^T (K = N); bf16 reads the hi plane
-    g.P = cbf16 ? Xh[cur] : static_cast<void*>(Xf);
-    g.Q = g.P;
-    g.sP = g.sQ = MN; g.ldp = g.ldq = L.N; g.K = L.N;
+    // the Gram and polynomial launches: lower-triangle tiles of M x M
     g.tiles_m = g.tiles_n = L.M / tile_sym; g.tri = 1;
-    g.C = A; g.sC = MM; g.ldc = L.M;
-    err = timed(MUON_K_GRAM, L.m, L.n, c.cnt, k, cnt * 2.0 * m * m * n,
-                pmn * es + pmm * es, s,
-                [&] { return launch_gemm(cbf16, EPI_GRAM, tile_sym, g, c.wt, c.cnt, s); });
-    if (err != hipSuccess) return MUON_ERR_HIP;
+
+    if (L.qaq && qaq_step(k, n_steps)) {
+      // A = Q A Q with the previous step's A (hi + residual) and B,
+      // Q = a_{k-1} I + B: T = a A + B A, then A = a T + T B.  Both products
+      // are symmetric (Q and A commute), so the POLY kernel forms them from
+      // their lower-triangle tiles; B and A, T are symmetric, so B^T = B and
+      // A^T = A as its second operand.  Counted as the Gram's flops, half
+      // per launch.
+      GemmArgs q = g;
+      q.inv = nullptr;
+      q.b = coeffs[k - 1].a; q.c = 1.f;
+      q.K = L.M; q.sP = q.sQ = MM; q.ldp = q.ldq = L.M;
+      q.sC = MM; q.ldc = L.M; q.sAin = MM;
+      q.P = B; q.Q = A; q.Ain = A; q.Alo = Alo; q.C = Tq;
+      err = timed(MUON_K_GRAMQ, L.m, L.n, c.cnt, k, cnt * m * m * n, 5.0 * pmm * es, s,
+                  [&] { return launch_gemm(cbf16, EPI_POLY_LO, tile_sym, q, c.wt, c.cnt, s); });
+      if (err != hipSuccess) return MUON_ERR_HIP;
+      q.P = Tq; q.Q = B; q.Ain = Tq; q.Alo = nullptr; q.C = A;
+      err = timed(MUON_K_GRAMQ, L.m, L.n, c.cnt, k, cnt * m * m * n, 4.0 * pmm * es, s,
+                  [&] { return launch_gemm(cbf16, EPI_POLY, tile_sym, q, c.wt, c.cnt, s); });
+      if (err != hipSuccess) return MUON_ERR_HIP;
+    } else {
+      // A = X X^T (K = N); bf16 reads the hi plane.  Before a step whose
+      // Gram matrix is Q A Q, A's residual is kept as well.
+      g.P = cbf16 ? Xh[cur] : static_cast<void*>(Xf);
+      g.Q = g.P;
+      g.sP = g.sQ = MN; g.ldp = g.ldq = L.N; g.K = L.N;
+      g.C = A; g.sC = MM; g.ldc = L.M;
+      g.Clo = L.qaq && qaq_step(k + 1, n_steps) ? Alo : nullptr;
+      err = timed(MUON_K_GRAM, L.m, L.n, c.cnt, k, cnt * 2.0 * m * m * n,
+                  pmn * es + pmm * es * (g.Clo ? 1.5 : 1.0), s,
+                  [&] {
+                    return launch_gemm(cbf16, g.Clo ? EPI_GRAM_LO : EPI_GRAM, tile_sym, g, c.wt,
+                                       c.cnt, s);
+                  });
+      if (err != hipSuccess) return MUON_ERR_HIP;
+      g.Clo = nullptr;
+    }
 
     // B = b A + c A A (K = M)
     g.inv = nullptr;

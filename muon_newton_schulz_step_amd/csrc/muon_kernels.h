@@ -21,7 +21,9 @@ constexpr int kPrepTile = 64;
 // matrices (stored transposed to the oriented X).
 enum Epi {
   EPI_GRAM = 0, EPI_POLY = 1, EPI_UPDATE = 2, EPI_FINAL_W = 3, EPI_FINAL_OUT = 4,
-  EPI_FINAL_W_T = 5, EPI_FINAL_OUT_T = 6
+  EPI_FINAL_W_T = 5, EPI_FINAL_OUT_T = 6,
+  EPI_GRAM_LO = 7,  // bf16 GRAM that also writes C's residual to Clo
+  EPI_POLY_LO = 8   // bf16 POLY whose A input is Ain + Alo
 };
 enum Final { FINAL_NONE = 0, FINAL_OUT = 1, FINAL_WEIGHTS = 2 };
 
@@ -70,6 +72,8 @@ struct GemmArgs {
   // GRAM / POLY output (M x M), POLY input A
   void* C; long long sC; int ldc;
   const void* Ain; long long sAin;
+  void* Clo;               // GRAM_LO: C's residual v - bf16(v), lower tiles only
+  const void* Alo;         // POLY_LO: a residual plane added to Ain (same layout)
   // UPDATE / FINAL: X state (see PrepArgs), leading dimension ldx, stride sX
   long long sX; int ldx;
   const void* Xh; void* Xh_next; void* Xl;  // bf16: hi (read), next hi, lo (in place)

@@ -9,8 +9,13 @@
 //   prep_kernel    momentum + Frobenius partial sums + oriented, zero-padded X_0
 //   norm_kernel    fixed-order reduction of the partials -> 1/(||u||_F + eps)
 //   gemm_kernel    C[i][j] = sum_k P[i][k] Q[j][k] on MFMA, epilogues:
-//                    GRAM   A = X X^T        (lower-triangle tiles, mirrored)
-//                    POLY   B = b A + c A A  (A symmetric, so A A = A A^T)
+//                    GRAM   A = X X^T        (lower-triangle tiles, mirrored;
+//                                             GRAM_LO: also A's bf16 residual
+//                                             on the lower tiles)
+//                    POLY   B = b A + c A A  (A symmetric, so A A = A A^T);
+//                           the same kernel forms A' = Q A Q, Q = aI + B,
+//                           as T = aA + B A (POLY_LO: A with its residual),
+//                           then A' = aT + T B
 //                    UPDATE X <- a X + B X   (bf16: Q is X's hi plane, read
 //                                             row-major and transposed in LDS;
 //                                             fp32: Q = X^T, kept as a copy)
@@ -398,7 +403,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
   constexpr bool FINAL = FIN_W || FIN_OUT;
   constexpr bool TALLF = EPI == EPI_FINAL_W_T || EPI == EPI_FINAL_OUT_T;  // FINAL, tall matrices
   constexpr bool HILO = sizeof(T) == 2;  // bf16 path: X state as hi + lo planes
-  constexpr bool STAGED_T = EPI == EPI_GRAM || EPI == EPI_POLY || (EPI == EPI_UPDATE && !HILO);
+  constexpr bool GRAMK = EPI == EPI_GRAM || EPI == EPI_GRAM_LO;
+  constexpr bool POLYK = EPI == EPI_POLY || EPI == EPI_POLY_LO;
+  constexpr bool STAGED_T = GRAMK || POLYK || (EPI == EPI_UPDATE && !HILO);
   static_assert(FM * 32 * WGM == BM && FN * 32 * WGN == BN, "wave tiles must be 32-aligned");
   static_assert(S == 0 || S == 2, "main loop variants");
   static_assert(!QROW || (HILO && BK == 64 && !STAGED_T), "row-major Q is the bf16 X operand");
@@ -651,10 +658,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
   // diagonal) or, on the fp32 path, the next step's X^T (UPDATE).
   bool stage_t = false;
   if constexpr (EPI == EPI_UPDATE) stage_t = STAGED_T;
-  if constexpr (EPI == EPI_GRAM || EPI == EPI_POLY) stage_t = ti != tj;
+  if constexpr (GRAMK || POLYK) stage_t = ti != tj;
   T* __restrict__ Ts = reinterpret_cast<T*>(smem);
   T* __restrict__ C = nullptr;
+  T* __restrict__ Clo = nullptr;  // GRAM: the residual of the stored tile, if asked for
   const T* __restrict__ Ain = nullptr;
+  const T* __restrict__ Alo = nullptr;  // POLY: a residual plane added to Ain, if given
   float* __restrict__ Xf = nullptr;
   const bf16_t* __restrict__ Xh = nullptr;
   bf16_t* __restrict__ Xh_next = nullptr;
@@ -676,7 +685,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
     }
   } else {
     C = static_cast<T*>(a.C) + (long long)mat * a.sC;
-    if constexpr (EPI == EPI_POLY) Ain = static_cast<const T*>(a.Ain) + (long long)mat * a.sAin;
+    if constexpr (EPI == EPI_GRAM_LO) Clo = static_cast<T*>(a.Clo) + (long long)mat * a.sC;
+    if constexpr (POLYK) Ain = static_cast<const T*>(a.Ain) + (long long)mat * a.sAin;
+    if constexpr (EPI == EPI_POLY_LO) Alo = static_cast<const T*>(a.Alo) + (long long)mat * a.sAin;
   }
   const int jl0 = wn * WTN + (lane & 31);
 
@@ -972,7 +983,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
       const int j = j_base + (n0 + nn) * 32 + (lane & 31);
       static_for<4 * EPQ>([&](auto e) {
         const int i = ib + 8 * (q0 + e / 4) + (e % 4);
-        if constexpr (EPI == EPI_POLY) ein[nn][e] = to_f32(Ain[(long long)i * a.ldc + j]);
+        if constexpr (POLYK) ein[nn][e] = to_f32(Ain[(long long)i * a.ldc + j]);
+        if constexpr (EPI == EPI_POLY_LO) ein[nn][e] += to_f32(Alo[(long long)i * a.ldc + j]);
         if constexpr (EPI == EPI_UPDATE || FINAL) {
           const long long o = (long long)i * a.ldx + j;
           if constexpr (HILO) ein[nn][e] = to_f32(Xh[o]) + to_f32(Xl[o]);
@@ -998,10 +1010,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
           constexpr int e = 4 * decltype(qq)::value + t;  // input of this pass
           const int i = ib + 8 * q + t;
           const float accv = acc[mi][ni][r];
-          if constexpr (EPI == EPI_GRAM) {
+          if constexpr (GRAMK) {
             v[t] = accv * alpha;
-            C[(long long)i * a.ldc + j] = from_f32<T>(v[t]);
-          } else if constexpr (EPI == EPI_POLY) {
+            const T hi = from_f32<T>(v[t]);
+            C[(long long)i * a.ldc + j] = hi;
+            if constexpr (EPI == EPI_GRAM_LO)
+              Clo[(long long)i * a.ldc + j] = from_f32<T>(v[t] - to_f32(hi));
+          } else if constexpr (POLYK) {
             v[t] = a.b * ein[nn][e] + a.c * accv;
             C[(long long)i * a.ldc + j] = from_f32<T>(v[t]);
           } else if constexpr (EPI == EPI_UPDATE) {
@@ -1252,7 +1267,8 @@ template <typename T, int E>
 static void launch_gemm_t(int tile, const GemmArgs& a, const WeightTable& t, dim3 grid,
                           hipStream_t s) {
   const GemmLaunch launch{a, t};
-  constexpr bool QR = sizeof(T) == 2 && E != EPI_GRAM && E != EPI_POLY;
+  constexpr bool QR = sizeof(T) == 2 && E != EPI_GRAM && E != EPI_POLY && E != EPI_GRAM_LO &&
+                     E != EPI_POLY_LO;
   if constexpr (sizeof(T) == 2) {
     // buffer loads address an operand panel with 32-bit lane offsets: up to
     // `tile` rows of the leading dimension
@@ -1288,6 +1304,8 @@ hipError_t launch_gemm(int compute_bf16, int epi, int tile, const GemmArgs& a_in
   if (compute_bf16) {
     if (epi == EPI_GRAM) launch_gemm_t<bf16_t, EPI_GRAM>(tile, a, t, grid, s);
     else if (epi == EPI_POLY) launch_gemm_t<bf16_t, EPI_POLY>(tile, a, t, grid, s);
+    else if (epi == EPI_GRAM_LO) launch_gemm_t<bf16_t, EPI_GRAM_LO>(tile, a, t, grid, s);
+    else if (epi == EPI_POLY_LO) launch_gemm_t<bf16_t, EPI_POLY_LO>(tile, a, t, grid, s);
     else if (epi == EPI_UPDATE) launch_gemm_t<bf16_t, EPI_UPDATE>(tile, a, t, grid, s);
     else if (epi == EPI_FINAL_W) launch_gemm_t<bf16_t, EPI_FINAL_W>(tile, a, t, grid, s);
     else if (epi == EPI_FINAL_OUT) launch_gemm_t<bf16_t, EPI_FINAL_OUT>(tile, a, t, grid, s);

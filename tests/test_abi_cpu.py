@@ -203,9 +203,12 @@ def test_workspace_sizes():
               (12288, 3072), (3072, 12288)] * 28
     ws = mn.step_workspace_bytes(shapes)
     assert ws == lib.muon_orthogonalize_workspace_bytes(56, 3072, 12288, 0)
-    # bf16: X as hi (twice) and lo planes, 2 bytes each, A and B (bf16), the
-    # fp32 norm partials of 64 x 64 tiles and the per-matrix 1/norm
-    need = 56 * (3 * 3072 * 12288 * 2 + 2 * 3072 * 3072 * 2 + (3072 // 64) * (12288 // 64) * 4 + 4)
+    # bf16: X as hi (twice) and lo planes, 2 bytes each, A and B (bf16), A's
+    # residual and the product T of the Q A Q steps (bf16; this group has
+    # N = 4M and M >= 2048), the fp32 norm partials of 64 x 64 tiles and the
+    # per-matrix 1/norm
+    need = 56 * (3 * 3072 * 12288 * 2 + 4 * 3072 * 3072 * 2
+                 + (3072 // 64) * (12288 // 64) * 4 + 4)
     assert need <= ws < need + 8 * 256
 
 

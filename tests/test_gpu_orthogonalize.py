@@ -214,3 +214,20 @@ def test_tall_batch_stride_through_c_abi(compute, out_dtype, pad):
         assert oracle.relative_frobenius_error(to64(o), ref) <= tol(compute) + extra, b
         if pad:  # the gap between matrices is not written
             assert torch.all(out[b * stride + rows * cols:(b + 1) * stride] == 7.0)
+
+
+@pytest.mark.parametrize("tall", [False, True], ids=["wide", "tall"])
+def test_gram_by_qaq_log_spectrum(tall):
+    # 2048 x 8192 is the smallest shape whose steps 1 and 3 form the Gram
+    # matrix as Q A Q (bf16, N >= 4M, M >= 2048); a log-uniform spectrum over
+    # four decades is where that rounding shows most (emulated: 7.5e-3 against
+    # 5.3e-3 for the Gram of X itself at 512 x 2048)
+    import dataclasses
+    announce("gram by QAQ, log spectrum 2048x8192", "tall" if tall else "wide")
+    w = dataclasses.replace(wl.STRESS_4096x16384, shapes=((8192, 2048) if tall else (2048, 8192),))
+    g = wl.make_grad(w, 0, device=DEV)
+    o = mn.orthogonalize(g, Q5, compute="bf16", out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    err = oracle.relative_frobenius_error(to64(o), oracle.orthogonalize(to64(g), Q5))
+    print("  rel err", err, flush=True)
+    assert err <= tol("bf16")
