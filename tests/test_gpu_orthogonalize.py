@@ -231,3 +231,16 @@ def test_gram_by_qaq_log_spectrum(tall):
     err = oracle.relative_frobenius_error(to64(o), oracle.orthogonalize(to64(g), Q5))
     print("  rel err", err, flush=True)
     assert err <= tol("bf16")
+
+
+def test_gram_by_qaq_per_step_table():
+    # Q = a_{k-1} I + B_{k-1} takes the previous step's a: with a table whose
+    # consecutive a differ (quintic, cubic, ...) a wrong step index would show
+    announce("gram by QAQ, per-step table, 2048x8192")
+    table = [wl.QUINTIC, wl.CUBIC, wl.QUINTIC, wl.CUBIC, wl.QUINTIC]
+    g = wl.gaussian_matrix(2048, 8192, seed=41, device=DEV).to(torch.bfloat16)
+    o = mn.orthogonalize(g, table, compute="bf16", out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    err = oracle.relative_frobenius_error(to64(o), oracle.orthogonalize(to64(g), table))
+    print("  rel err", err, flush=True)
+    assert err <= tol("bf16")
