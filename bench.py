@@ -133,6 +133,37 @@ def launch_sequence(w):
     return seq
 
 
+def ns_flops_executed(w, compute="bf16"):
+    """Flops the GEMM launches of one step execute (MFMA work over the padded
+    tiles they run), against the method's counted 4m^2n + 2m^3 per matrix
+    and step: GRAM and POLY run lower-triangle tiles only, and on the bf16
+    path the Gram matrix of steps 1 and 3 of groups with padded N >= 4M and
+    M >= 2048 is formed as Q A Q (two M x M x M triangle launches)."""
+    def pad(d):
+        return (d + 255) // 256 * 256
+    groups = {}
+    for r, c in w.shapes:
+        key = (min(r, c), max(r, c))
+        groups[key] = groups.get(key, 0) + 1
+    tot = 0.0
+    for (m, n), count in groups.items():
+        M, N = pad(m), pad(n)
+        for b0 in range(0, count, 64):
+            cnt = min(64, count - b0)
+            t256 = M // 256
+            tile = 256 if compute == "bf16" and t256 * (t256 + 1) // 2 * cnt >= 512 else 128
+            tri = (M // tile) * (M // tile + 1) // 2 * tile * tile * cnt  # C elements computed
+            qaq = compute == "bf16" and N >= 4 * M and M >= 2048
+            for k in range(w.n_steps):
+                if qaq and k in (1, 3) and k <= w.n_steps - 2:
+                    tot += 2 * (2.0 * tri * M)
+                else:
+                    tot += 2.0 * tri * N
+                tot += 2.0 * tri * M                   # POLY
+                tot += 2.0 * M * N * M * cnt           # UPDATE / FINAL (full tiles)
+    return tot
+
+
 def write_traffic(fetch_csv, write_csv, w):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of one profiled step,
     scaled by what the same counters read for a plain copy kernel of
@@ -360,6 +391,8 @@ def main():
         "ns_frac_of_peak": round(ns_tflops / PEAK[args.compute], 4),
         "step_tflops": round(step_tflops, 2),
         "counted_ns_tflop_per_step": round(flops / 1e12, 3),
+        "executed_ns_tflop_per_step": round(ns_flops_executed(w, args.compute) / 1e12, 3),
+        "ns_tflops_executed": round(ns_flops_executed(w, args.compute) / (ns_ms * 1e-3) / 1e12, 2),
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": [{k2: (round(v, 4) if isinstance(v, float) else v) for k2, v in k.items()
