@@ -62,14 +62,16 @@ int pick_tile(bool cbf16, long long tiles_at_256, int batch) {
 //   bf16: hi plane twice (the update reads one, writes the other), lo plane;
 //   fp32: X, X^T twice (read by the update, written by it).
 // Then A and B (M x M, compute precision), the norm partials and 1/norm,
-// and with NorMuon the per-row scales 1/(sqrt(v') + eps) (M floats).  Groups
+// and with NorMuon the per-row scales 1/(sqrt(v') + eps) (M floats) and, on
+// the bf16 path, the last update's row sums (N / 64 blocks of M floats).  Groups
 // that form some Gram matrices as Q A Q (gram_by_qaq) add A's residual and
 // the product T (M x M bf16 each).
 struct Layout {
   int m = 0, n = 0, M = 0, N = 0, cnt = 0, nblk = 0;
   bool qaq = false;
   size_t x0 = 0, x1 = 0, x2 = 0, A = 0, B = 0, Alo = 0, T = 0, part = 0, inv = 0, rinv = 0,
-         total = 0;
+         rowpart = 0, total = 0;
+  bool rowsums = false;
 };
 
 // The Gram matrix of the next step is Q A Q, Q = aI + B (X' = Q X, so
@@ -109,6 +111,8 @@ bool make_layout(int cnt, int m, int n, bool cbf16, Layout& L, bool normuon = fa
   L.part = take((size_t)cnt * (size_t)L.nblk * 4);
   L.inv = take((size_t)cnt * 4);
   if (normuon) L.rinv = take((size_t)cnt * (size_t)M * 4);
+  L.rowsums = normuon && cbf16;
+  if (L.rowsums) L.rowpart = take((size_t)cnt * (size_t)(N / 64) * (size_t)M * 4);
   L.total = off;
   return true;
 }
@@ -324,11 +328,20 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
     // X) and writes the next X (bf16: hi + lo, fp32: X + X^T), or, on the
     // last step, reads and writes the weights or writes the output
     if (!last || c.normuon) {
-      // (with NorMuon the last step is a plain update too; the weights
-      // follow in their own passes below)
-      const double upd_bytes = pmm * es + pmn * es + pmn * 4.0 + pmn * (cbf16 ? 4.0 : 8.0);
-      err = timed(MUON_K_UPDATE, L.m, L.n, c.cnt, k, cnt * 2.0 * m * m * n, upd_bytes, s,
-                  [&] { return launch_gemm(cbf16, EPI_UPDATE, tile_upd, g, c.wt, c.cnt, s); });
+      // (with NorMuon the last step is a plain update too, on the bf16 path
+      // with the row sums of the result; the weights follow in their own
+      // passes below)
+      const bool rows = last && L.rowsums;
+      if (rows) {
+        g.rowpart = reinterpret_cast<float*>(ws + L.rowpart);
+        g.ld_rp = L.M;
+        g.s_rp = (long long)(L.N / 64) * L.M;
+      }
+      const double upd_bytes = pmm * es + pmn * es + pmn * 4.0 + pmn * (cbf16 ? 4.0 : 8.0) +
+                               (rows ? pmn / 16.0 : 0.0);
+      err = timed(MUON_K_UPDATE, L.m, L.n, c.cnt, k, cnt * 2.0 * m * m * n, upd_bytes, s, [&] {
+        return launch_gemm(cbf16, rows ? EPI_UPDATE_ROWS : EPI_UPDATE, tile_upd, g, c.wt, c.cnt, s);
+      });
     } else {
       // The chunk holds its wide matrices first, then the tall ones, which
       // store the result transposed; each part has its own launch.
@@ -359,9 +372,15 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
     na.m = L.m; na.n = L.n; na.M = L.M; na.N = L.N;
     na.sX = MN; na.ldx = L.N;
     na.Xh = Xh[n_steps & 1]; na.Xl = Xl; na.Xf = Xf;
+    if (L.rowsums) {
+      na.rowpart = reinterpret_cast<const float*>(ws + L.rowpart);
+      na.ld_rp = L.M;
+      na.s_rp = (long long)(L.N / 64) * L.M;
+    }
     na.beta2 = c.beta2; na.eps2 = c.eps2;
     na.rinv = rinv;
-    err = timed(MUON_K_NORMUON, L.m, L.n, c.cnt, -1, 0.0, pmn * 4.0 + cnt * L.m * 8.0, s,
+    const double rows_read = L.rowsums ? pmn / 16.0 : pmn * 4.0;
+    err = timed(MUON_K_NORMUON, L.m, L.n, c.cnt, -1, 0.0, rows_read + cnt * L.m * 8.0, s,
                 [&] { return launch_normuon_rows(cbf16, na, c.vt, c.cnt, s); });
     if (err != hipSuccess) return MUON_ERR_HIP;
     ApplyArgs aa{};

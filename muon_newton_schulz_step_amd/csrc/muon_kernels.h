@@ -23,7 +23,8 @@ enum Epi {
   EPI_GRAM = 0, EPI_POLY = 1, EPI_UPDATE = 2, EPI_FINAL_W = 3, EPI_FINAL_OUT = 4,
   EPI_FINAL_W_T = 5, EPI_FINAL_OUT_T = 6,
   EPI_GRAM_LO = 7,  // bf16 GRAM that also writes C's residual to Clo
-  EPI_POLY_LO = 8   // bf16 POLY whose A input is Ain + Alo
+  EPI_POLY_LO = 8,  // bf16 POLY whose A input is Ain + Alo
+  EPI_UPDATE_ROWS = 9  // bf16 UPDATE that also writes row sums of the new X^2
 };
 enum Final { FINAL_NONE = 0, FINAL_OUT = 1, FINAL_WEIGHTS = 2 };
 
@@ -90,6 +91,9 @@ struct GemmArgs {
   float neg_lrwd;          // FINAL_W: -lr * weight_decay (0: no decay)
   int cautious;            // FINAL_W: decay only where O * W >= 0
   float neg_lr;
+  // UPDATE_ROWS: sum over each 64-column block jb of X'[i][j]^2 at
+  // rowpart[mat * s_rp + jb * ld_rp + i]
+  float* rowpart; long long s_rp; int ld_rp;
 };
 
 struct WeightTable {       // FINAL_WEIGHTS only
@@ -119,6 +123,9 @@ struct NormuonArgs {
   long long sX; int ldx;   // X state as in GemmArgs
   const void* Xh; const void* Xl;  // bf16: hi, lo
   const float* Xf;                 // fp32: X
+  // bf16: the last UPDATE's row sums (GemmArgs::rowpart), N / 64 per row,
+  // summed here instead of reading X
+  const float* rowpart; long long s_rp; int ld_rp;
   float beta2, eps2;
   float* rinv;             // [matrix][M]
 };

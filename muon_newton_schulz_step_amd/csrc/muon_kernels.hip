@@ -18,11 +18,14 @@
 //                           then A' = aT + T B
 //                    UPDATE X <- a X + B X   (bf16: Q is X's hi plane, read
 //                                             row-major and transposed in LDS;
-//                                             fp32: Q = X^T, kept as a copy)
+//                                             fp32: Q = X^T, kept as a copy;
+//                                             UPDATE_ROWS: also each row's sum
+//                                             of X'^2 per 64-column block)
 //                    FINAL  the last UPDATE, into the weights (with page 1's
 //                           decoupled or cautious weight decay) or the output
 //   normuon_rows_kernel  NorMuon (page 1): per oriented row, the mean of O^2,
 //                        the second-moment update and the row's scale
+//                        (bf16: normuon_rowparts_kernel, from UPDATE_ROWS' sums)
 //   apply_kernel         with NorMuon, the weight update as its own pass
 // The 1/||u|| normalisation is folded into the first GRAM (x inv^2) and
 // UPDATE (x inv) epilogues.
@@ -405,7 +408,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
   constexpr bool HILO = sizeof(T) == 2;  // bf16 path: X state as hi + lo planes
   constexpr bool GRAMK = EPI == EPI_GRAM || EPI == EPI_GRAM_LO;
   constexpr bool POLYK = EPI == EPI_POLY || EPI == EPI_POLY_LO;
-  constexpr bool STAGED_T = GRAMK || POLYK || (EPI == EPI_UPDATE && !HILO);
+  constexpr bool UPD = EPI == EPI_UPDATE || EPI == EPI_UPDATE_ROWS;
+  constexpr bool ROWS = EPI == EPI_UPDATE_ROWS;
+  static_assert(!ROWS || HILO, "row sums on the bf16 path");
+  constexpr bool STAGED_T = GRAMK || POLYK || (UPD && !HILO);
   static_assert(FM * 32 * WGM == BM && FN * 32 * WGN == BN, "wave tiles must be 32-aligned");
   static_assert(S == 0 || S == 2, "main loop variants");
   static_assert(!QROW || (HILO && BK == 64 && !STAGED_T), "row-major Q is the bf16 X operand");
@@ -657,7 +663,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
   // Transposed output of this block: the mirrored tile (GRAM, POLY off the
   // diagonal) or, on the fp32 path, the next step's X^T (UPDATE).
   bool stage_t = false;
-  if constexpr (EPI == EPI_UPDATE) stage_t = STAGED_T;
+  if constexpr (UPD) stage_t = STAGED_T;
   if constexpr (GRAMK || POLYK) stage_t = ti != tj;
   T* __restrict__ Ts = reinterpret_cast<T*>(smem);
   T* __restrict__ C = nullptr;
@@ -670,11 +676,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
   bf16_t* __restrict__ Xl = nullptr;
   float* __restrict__ W = nullptr;
   float wscale = 0.f;
-  if constexpr (EPI == EPI_UPDATE || FINAL) {
+  if constexpr (UPD || FINAL) {
     if constexpr (HILO) {
       Xh = static_cast<const bf16_t*>(a.Xh) + (long long)mat * a.sX;
       Xl = static_cast<bf16_t*>(a.Xl) + (long long)mat * a.sX;
-      if constexpr (EPI == EPI_UPDATE)
+      if constexpr (UPD)
         Xh_next = static_cast<bf16_t*>(a.Xh_next) + (long long)mat * a.sX;
     } else {
       Xf = a.Xf + (long long)mat * a.sX;
@@ -817,7 +823,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
   // reads them back as runs; the next block's hi and lo are loaded while this
   // one is staged.  Only the wave itself touches its area and a wave's LDS
   // accesses execute in issue order, so a compiler barrier orders them.
-  if constexpr ((EPI == EPI_UPDATE || (FINAL && !TALLF)) && HILO) {
+  if constexpr ((UPD || (FINAL && !TALLF)) && HILO) {
     constexpr int RPL = WTN / 8;         // runs per staged row
     constexpr int RSTEP = 64 / RPL;      // rows between a lane's runs
     constexpr int RUNS = 32 / RSTEP;     // runs per lane and block
@@ -938,6 +944,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
           }
         } else {
         u32x4_t ho, lo;
+        [[maybe_unused]] float ss = 0.f;
         static_for<4>([&](auto w) {
           const unsigned hw = hv[b][s][(int)w], lw = lv[b][s][(int)w];
           unsigned short hb[2], lb[2];
@@ -946,8 +953,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
             const float x = __uint_as_float(h ? hw & 0xffff0000u : hw << 16) +
                             __uint_as_float(h ? lw & 0xffff0000u : lw << 16);
             const float accv = e < 4 ? p0[e & 3] : p1[e & 3];
+            const float xn = scl * (a.a * x + accv);
+            if constexpr (ROWS) ss = fmaf(xn, xn, ss);
             bf16_t vh, vl;
-            split_bf16(scl * (a.a * x + accv), vh, vl);
+            split_bf16(xn, vh, vl);
             hb[h] = __builtin_bit_cast(unsigned short, vh);
             lb[h] = __builtin_bit_cast(unsigned short, vl);
           });
@@ -958,6 +967,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
         // lo is updated in place: only this block reads X[i][j]'s lo
         *reinterpret_cast<u32x4_t*>(Xh_next + o) = ho;
         *reinterpret_cast<u32x4_t*>(Xl + o) = lo;
+        if constexpr (ROWS) {
+          // the row's sum over the wave's 64 columns, from the 8 lanes of
+          // its runs in a fixed butterfly order (all lanes are active here)
+          ss += __shfl_xor(ss, 1);
+          ss += __shfl_xor(ss, 2);
+          ss += __shfl_xor(ss, 4);
+          if (lane % RPL == 0)
+            a.rowpart[(long long)mat * a.s_rp + (long long)(j_base / WTN) * a.ld_rp + i_base +
+                      mi * 32 + rr0 + RSTEP * s] = ss;
+        }
         }
       });
       asm volatile("" ::: "memory");  // this block's reads before the next one's writes
@@ -985,7 +1004,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
         const int i = ib + 8 * (q0 + e / 4) + (e % 4);
         if constexpr (POLYK) ein[nn][e] = to_f32(Ain[(long long)i * a.ldc + j]);
         if constexpr (EPI == EPI_POLY_LO) ein[nn][e] += to_f32(Alo[(long long)i * a.ldc + j]);
-        if constexpr (EPI == EPI_UPDATE || FINAL) {
+        if constexpr (UPD || FINAL) {
           const long long o = (long long)i * a.ldx + j;
           if constexpr (HILO) ein[nn][e] = to_f32(Xh[o]) + to_f32(Xl[o]);
           else ein[nn][e] = Xf[o];
@@ -1019,7 +1038,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
           } else if constexpr (POLYK) {
             v[t] = a.b * ein[nn][e] + a.c * accv;
             C[(long long)i * a.ldc + j] = from_f32<T>(v[t]);
-          } else if constexpr (EPI == EPI_UPDATE) {
+          } else if constexpr (UPD) {
             v[t] = scl * (a.a * ein[nn][e] + accv);
             const long long o = (long long)i * a.ldx + j;
             if constexpr (HILO) {
@@ -1070,7 +1089,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
       __syncthreads();
       T* __restrict__ dst;
       int ld;
-      if constexpr (EPI == EPI_UPDATE) {
+      if constexpr (UPD) {
         dst = static_cast<T*>(a.XTo) + (long long)mat * a.sXT;
         ld = a.ldxt;
       } else {
@@ -1135,6 +1154,25 @@ __global__ __launch_bounds__(256) void normuon_rows_kernel(NormuonLaunch launch)
     }
     a.rinv[(long long)mat * a.M + i] = r;
   }
+}
+
+// The same from the row sums that the last bf16 UPDATE left per 64-column
+// block: one thread per oriented row, the blocks added in column order.
+__global__ __launch_bounds__(256) void normuon_rowparts_kernel(NormuonLaunch launch) {
+  const NormuonArgs& a = launch.a;
+  const int i = blockIdx.x * 256 + threadIdx.x, mat = blockIdx.y;
+  const float* p = a.rowpart + (long long)mat * a.s_rp + i;
+  const int nb = a.N / 64;
+  float total = 0.f;
+  for (int jb = 0; jb < nb; ++jb) total += p[(long long)jb * a.ld_rp];
+  float r = 0.f;
+  if (i < a.m) {
+    float* v = kernarg<NormuonLaunch>().t.v[mat];
+    const float nv = a.beta2 * v[i] + (1.f - a.beta2) * (total / (float)a.n);
+    v[i] = nv;
+    r = 1.f / (sqrtf(nv) + a.eps2);
+  }
+  a.rinv[(long long)mat * a.M + i] = r;
 }
 
 // The weight update as its own pass: one 64x64 tile of the oriented, padded
@@ -1223,7 +1261,9 @@ hipError_t launch_norm(const float* partials, int nblk, float eps, float* inv, i
 hipError_t launch_normuon_rows(int compute_bf16, const NormuonArgs& a, const RowTable& t,
                                int batch, hipStream_t s) {
   const NormuonLaunch launch{a, t};
-  if (compute_bf16)
+  if (compute_bf16 && a.rowpart)
+    hipLaunchKernelGGL(normuon_rowparts_kernel, dim3(a.M / 256, batch), dim3(256), 0, s, launch);
+  else if (compute_bf16)
     hipLaunchKernelGGL(normuon_rows_kernel<true>, dim3(a.M, batch), dim3(256), 0, s, launch);
   else
     hipLaunchKernelGGL(normuon_rows_kernel<false>, dim3(a.M, batch), dim3(256), 0, s, launch);
@@ -1307,6 +1347,7 @@ hipError_t launch_gemm(int compute_bf16, int epi, int tile, const GemmArgs& a_in
     else if (epi == EPI_GRAM_LO) launch_gemm_t<bf16_t, EPI_GRAM_LO>(tile, a, t, grid, s);
     else if (epi == EPI_POLY_LO) launch_gemm_t<bf16_t, EPI_POLY_LO>(tile, a, t, grid, s);
     else if (epi == EPI_UPDATE) launch_gemm_t<bf16_t, EPI_UPDATE>(tile, a, t, grid, s);
+    else if (epi == EPI_UPDATE_ROWS) launch_gemm_t<bf16_t, EPI_UPDATE_ROWS>(tile, a, t, grid, s);
     else if (epi == EPI_FINAL_W) launch_gemm_t<bf16_t, EPI_FINAL_W>(tile, a, t, grid, s);
     else if (epi == EPI_FINAL_OUT) launch_gemm_t<bf16_t, EPI_FINAL_OUT>(tile, a, t, grid, s);
     else if (epi == EPI_FINAL_W_T) launch_gemm_t<bf16_t, EPI_FINAL_W_T>(tile, a, t, grid, s);

@@ -175,9 +175,13 @@ def test_step_ex_workspace_sizes():
     wd_only = _lib.MuonOptions(0.1, 1, 0, 0.0, 0.0)
     assert lib.muon_step_ex_workspace_bytes(3, r, c, 0, ctypes.byref(wd_only)) == plain
     nm = _lib.MuonOptions(0.0, 1, 1, 0.9, 1e-8)
-    # NorMuon adds the per-row scales of the largest group: 2 x (3072, 12288)
-    # (one wide, one tall), 3072 floats each, 256-byte aligned
-    assert lib.muon_step_ex_workspace_bytes(3, r, c, 0, ctypes.byref(nm)) == plain + 2 * 3072 * 4
+    # NorMuon adds, for the largest group, 2 x (3072, 12288) (one wide, one
+    # tall): the per-row scales (3072 floats each) and, on the bf16 path, the
+    # last update's row sums (12288 / 64 blocks of 3072 floats each)
+    assert lib.muon_step_ex_workspace_bytes(3, r, c, 0, ctypes.byref(nm)) == (
+        plain + 2 * 3072 * 4 + 2 * (12288 // 64) * 3072 * 4)
+    plain32 = lib.muon_step_workspace_bytes(3, r, c, 1)
+    assert lib.muon_step_ex_workspace_bytes(3, r, c, 1, ctypes.byref(nm)) == plain32 + 2 * 3072 * 4
     bad = _lib.MuonOptions(-1.0, 1, 0, 0.0, 0.0)
     assert lib.muon_step_ex_workspace_bytes(3, r, c, 0, ctypes.byref(bad)) == 0
     # with NorMuon the plain size is too small
