@@ -143,3 +143,41 @@ def test_gpt_3p8b_step_ex_sampled():
         assert oracle.relative_frobenius_error(dw_gpu, dw_ref) <= t, k
         assert oracle.relative_frobenius_error(to64(inp["bufs"][k]), ref["buf"]) <= BUF_TOL
         assert oracle.relative_frobenius_error(to64(vs[k]), ref["v"]) <= 2 * t
+
+
+@pytest.mark.parametrize("compute", ["bf16", "fp32"])
+def test_normuon_row_statistics_match_the_applied_update(compute):
+    """Each oriented row's second moment is the moving average of the mean
+    square of exactly the direction the same call applied to that row.
+
+    Without weight decay the call moves W by -lr*scale*O[i]/(sqrt(v'[i]) + eps),
+    so O is recovered from the weights and v' (to ~1e-7), and the mean of its
+    squares along the row must give v'.  This pins the row statistics at the
+    arithmetic's precision (the bf16 path sums the update's fp32 values, the
+    weights get its 16-bit hi + lo form: 2^-16 apart at most), where the
+    comparison with the oracle only bounds them by the Newton-Schulz error.
+    Eight 1024x4096 matrices run on 256-wide tiles (64 column blocks per
+    row), the ragged 300x1000 pair (one wide, one tall) on 128-wide ones."""
+    shapes = ((1024, 4096),) * 8 + ((300, 1000), (1000, 300))
+    beta2, eps = 0.5, 1e-8
+    announce("normuon row statistics", compute, shapes)
+    w = dataclasses.replace(wl.GPT_D768, shapes=shapes)
+    inp = wl.make_inputs(w, device=DEV)
+    vs = [wl.make_second_moment(w, i, device=DEV) for i in range(len(shapes))]
+    v0 = [to64(v) for v in vs]
+    before = [to64(p) for p in inp["params"]]
+    mn.step_ex(inp["params"], inp["grads"], inp["bufs"], mu=w.mu, lr=w.lr,
+               scales=inp["scales"], coeffs=w.coeff_table, compute=compute,
+               weight_decay=0.0, cautious=False, second_moments=vs, beta2=beta2,
+               normuon_eps=eps)
+    torch.cuda.synchronize()
+    for k, (r, c) in enumerate(shapes):
+        dw = to64(inp["params"][k]) - before[k]
+        if r > c:
+            dw = dw.T  # oriented: rows along the shorter side
+        v1 = to64(vs[k])
+        o = dw * (np.sqrt(v1) + eps)[:, None] / (-w.lr * inp["scales"][k])
+        mean_sq = np.mean(o ** 2, axis=1)
+        mean_gpu = (v1 - beta2 * v0[k]) / (1.0 - beta2)
+        rel = np.abs(mean_gpu - mean_sq) / mean_sq
+        assert rel.max() <= 1e-4, (k, (r, c), float(rel.max()), int(rel.argmax()))
