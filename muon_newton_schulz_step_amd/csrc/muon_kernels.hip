@@ -86,6 +86,15 @@ __device__ __forceinline__ float weight_step(float w, float x, float wscale, flo
   return decay ? fmaf(neg_lrwd, w, nw) : nw;
 }
 
+// Streaming (nontemporal) loads and stores, for data that a launch touches
+// once: the X state in the update and final epilogues, the weights, and the
+// gradient, momentum and X_0 of prep.  Kept out of the caches, they leave
+// L2 to the operand panels that the GEMM main loops re-read.
+template <typename V>
+__device__ __forceinline__ V ld_nt(const V* p) { return __builtin_nontemporal_load(p); }
+template <typename V>
+__device__ __forceinline__ void st_nt(V v, V* p) { __builtin_nontemporal_store(v, p); }
+
 // Compile-time loop: f(std::integral_constant<int, 0>) ... f(<N-1>), so that
 // register arrays are never indexed at run time (which would put them in
 // scratch memory).
@@ -143,8 +152,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepLaunch launch) {
     if constexpr (HILO) {
       bf16_t hi, lo;
       split_bf16(u, hi, lo);
-      Xh[o] = hi;
-      Xl[o] = lo;
+      st_nt(hi, Xh + o);
+      st_nt(lo, Xl + o);
     } else {
       Xf[o] = u;
     }
@@ -159,10 +168,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepLaunch launch) {
     float u = 0.f;
     if (r < rows && c < cols) {
       const long long idx = (long long)r * cols + c;
-      const float gv = to_f32(g[idx]);
+      const float gv = to_f32(ld_nt(g + idx));
       if constexpr (MOM) {
-        const float nb = a.mu * buf[idx] + gv;  // buf' = mu*buf + g
-        buf[idx] = nb;
+        const float nb = a.mu * ld_nt(buf + idx) + gv;  // buf' = mu*buf + g
+        st_nt(nb, buf + idx);
         u = gv + a.mu * nb;                     // u = g + mu*buf'
       } else {
         u = gv;
@@ -719,7 +728,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
           float ein[16];
           static_for<16>([&](auto r) {
             const long long o = (long long)(ib + 8 * (r / 4) + (r % 4)) * a.ldx + j;
-            if constexpr (HILO) ein[r] = to_f32(Xh[o]) + to_f32(Xl[o]);
+            if constexpr (HILO) ein[r] = to_f32(ld_nt(Xh + o)) + to_f32(ld_nt(Xl + o));
             else ein[r] = Xf[o];
           });
           const int jl = jl0 + ni * 32;
@@ -757,7 +766,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
 #pragma unroll
             for (int s = 0; s < HALF; ++s) {
               if (a.vec_tall && nval[s] == 4) {
-                wv[s] = *reinterpret_cast<const f32x4_t*>(W + off[s]);
+                wv[s] = ld_nt(reinterpret_cast<const f32x4_t*>(W + off[s]));
               } else {
 #pragma unroll
                 for (int t = 0; t < 4; ++t) wv[s][t] = t < nval[s] ? W[off[s] + t] : 0.f;
@@ -770,7 +779,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
               for (int t = 0; t < 4; ++t)
               w[t] = weight_step(wv[s][t], xv[s][t], wscale, a.neg_lrwd, a.cautious);
               if (a.vec_tall && nval[s] == 4) {
-                *reinterpret_cast<f32x4_t*>(W + off[s]) = w;
+                st_nt(w, reinterpret_cast<f32x4_t*>(W + off[s]));
               } else {
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
@@ -845,8 +854,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
     auto load = [&](auto mi, auto b) __attribute__((always_inline)) {
       static_for<RUNS>([&](auto s) {
         const long long o = offset(decltype(mi)::value, s);
-        hv[decltype(b)::value][s] = *reinterpret_cast<const u32x4_t*>(Xh + o);
-        lv[decltype(b)::value][s] = *reinterpret_cast<const u32x4_t*>(Xl + o);
+        hv[decltype(b)::value][s] = ld_nt(reinterpret_cast<const u32x4_t*>(Xh + o));
+        lv[decltype(b)::value][s] = ld_nt(reinterpret_cast<const u32x4_t*>(Xl + o));
       });
     };
     load(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
@@ -869,8 +878,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
           const int i = i_base + mi * 32 + rr0 + RSTEP * s, j = j_base + cc;
           const float* Wr = W + (long long)i * a.n + j;
           if (i < a.m && a.vec_wide && j + 8 <= a.n) {
-            wv[s][0] = *reinterpret_cast<const f32x4_t*>(Wr);
-            wv[s][1] = *reinterpret_cast<const f32x4_t*>(Wr + 4);
+            wv[s][0] = ld_nt(reinterpret_cast<const f32x4_t*>(Wr));
+            wv[s][1] = ld_nt(reinterpret_cast<const f32x4_t*>(Wr + 4));
           } else {
             static_for<8>([&](auto e) {
               wv[s][e / 4][e % 4] = i < a.m && j + e < a.n ? Wr[(int)e] : 0.f;
@@ -904,8 +913,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
                 w1[(int)t] = weight_step(wv[s][1][(int)t], x[4 + t], wscale, a.neg_lrwd, a.cautious);
               });
               if (full) {
-                *reinterpret_cast<f32x4_t*>(Wr) = w0;
-                *reinterpret_cast<f32x4_t*>(Wr + 4) = w1;
+                st_nt(w0, reinterpret_cast<f32x4_t*>(Wr));
+                st_nt(w1, reinterpret_cast<f32x4_t*>(Wr + 4));
               } else {
                 static_for<8>([&](auto e) {
                   if (j + e < a.n) Wr[(int)e] = e < 4 ? w0[e & 3] : w1[e & 3];
@@ -965,8 +974,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
         });
         const long long o = offset(mi, s);
         // lo is updated in place: only this block reads X[i][j]'s lo
-        *reinterpret_cast<u32x4_t*>(Xh_next + o) = ho;
-        *reinterpret_cast<u32x4_t*>(Xl + o) = lo;
+        st_nt(ho, reinterpret_cast<u32x4_t*>(Xh_next + o));
+        st_nt(lo, reinterpret_cast<u32x4_t*>(Xl + o));
         if constexpr (ROWS) {
           // the row's sum over the wave's 64 columns, from the 8 lanes of
           // its runs in a fixed butterfly order (all lanes are active here)
