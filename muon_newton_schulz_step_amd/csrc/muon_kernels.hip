@@ -87,8 +87,8 @@ __device__ __forceinline__ float weight_step(float w, float x, float wscale, flo
 }
 
 // Streaming (nontemporal) loads and stores, for data that a launch touches
-// once: the X state in the update and final epilogues, the weights, and the
-// gradient, momentum and X_0 of prep.  Kept out of the caches, they leave
+// once: the X state in the update and final epilogues and in NorMuon's
+// weight pass, the weights, and the gradient, momentum and X_0 of prep.  Kept out of the caches, they leave
 // L2 to the operand panels that the GEMM main loops re-read.
 template <typename V>
 __device__ __forceinline__ V ld_nt(const V* p) { return __builtin_nontemporal_load(p); }
@@ -1204,7 +1204,8 @@ __global__ __launch_bounds__(256) void apply_kernel(ApplyLaunch launch) {
     const long long o = base + (long long)oi * a.ldx + oj;
     float x;
     if constexpr (HILO) {
-      x = to_f32(static_cast<const bf16_t*>(a.Xh)[o]) + to_f32(static_cast<const bf16_t*>(a.Xl)[o]);
+      x = to_f32(ld_nt(static_cast<const bf16_t*>(a.Xh) + o)) +
+          to_f32(ld_nt(static_cast<const bf16_t*>(a.Xl) + o));
     } else {
       x = a.Xf[o];
     }
@@ -1218,7 +1219,7 @@ __global__ __launch_bounds__(256) void apply_kernel(ApplyLaunch launch) {
       if (oi < a.m && oj < a.n) {
         const float x = o_at(oi, oj);
         const long long idx = (long long)oi * a.n + oj;
-        W[idx] = weight_step(W[idx], x, wscale, a.neg_lrwd, a.cautious);
+        st_nt(weight_step(ld_nt(W + idx), x, wscale, a.neg_lrwd, a.cautious), W + idx);
       }
     }
   } else {
@@ -1231,7 +1232,7 @@ __global__ __launch_bounds__(256) void apply_kernel(ApplyLaunch launch) {
       const int r = oj0 + lc, c = oi0 + cc;  // original (row, col) of oriented (c, r)
       if (r < a.n && c < a.m) {
         const long long idx = (long long)r * a.m + c;
-        W[idx] = weight_step(W[idx], tile[cc][lc], wscale, a.neg_lrwd, a.cautious);
+        st_nt(weight_step(ld_nt(W + idx), tile[cc][lc], wscale, a.neg_lrwd, a.cautious), W + idx);
       }
     }
   }
