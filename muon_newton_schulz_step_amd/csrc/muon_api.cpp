@@ -85,6 +85,12 @@ bool gram_by_qaq(bool cbf16, long long M, long long N) { return cbf16 && N >= 4 
 // over more than one step.
 bool qaq_step(int k, int n_steps) { return (k == 1 || k == 3) && k <= n_steps - 2; }
 
+// Chunks whose X state is larger than the chip's 256 MB last-level cache
+// stream it: the UPDATE / FINAL epilogues and prep load and store the X
+// state, weights, gradient and momentum nontemporally, which leaves L2 to
+// the GEMM operand panels.  Smaller ones keep X cached for the next launch.
+constexpr double kStreamBytes = 256.0 * (1 << 20);
+
 bool make_layout(int cnt, int m, int n, bool cbf16, Layout& L, bool normuon = false) {
   const long long M = pad_dim(m), N = pad_dim(n);
   if (M * N > MUON_MAX_ELEMENTS) return false;
@@ -211,8 +217,11 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
   const double elems = m * n * cnt;
   const double pmn = cnt * (double)MN, pmm = cnt * (double)MM;  // padded elements
 
+  // X state: hi twice + lo (bf16), or X + X^T twice (fp32)
+  const bool stream = pmn * (cbf16 ? 6.0 : 12.0) > kStreamBytes;
   PrepArgs pa{};
   pa.m = L.m; pa.n = L.n; pa.M = L.M; pa.N = L.N;
+  pa.stream = stream;
   pa.tall_mask = c.tall_mask;
   pa.tiles_n = L.N / kPrepTile;
   pa.in = c.in; pa.s_in = c.s_in;
@@ -242,6 +251,7 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
     const bool first = k == 0, last = k == n_steps - 1;
     const int cur = k & 1;
     GemmArgs g{};
+    g.stream = stream;
     g.inv = first ? inv : nullptr;
     g.a = coeffs[k].a; g.b = coeffs[k].b; g.c = coeffs[k].c;
     g.m = L.m; g.n = L.n; g.tall_mask = c.tall_mask;

@@ -49,6 +49,7 @@ struct PrepArgs {
   void* XT; long long sXT; // fp32: X_0^T, N x M
   float* partials;         // [matrix][tile] sum of u^2
   int nblk;                // tiles per matrix
+  int stream;              // nontemporal accesses (the group's X state is large)
 };
 
 struct PrepTable {         // step only: per-matrix gradient / momentum pointers
@@ -91,6 +92,7 @@ struct GemmArgs {
   float neg_lrwd;          // FINAL_W: -lr * weight_decay (0: no decay)
   int cautious;            // FINAL_W: decay only where O * W >= 0
   float neg_lr;
+  int stream;              // UPDATE / FINAL: nontemporal X-state and weight accesses
   // UPDATE_ROWS: sum over each 64-column block jb of X'[i][j]^2 at
   // rowpart[mat * s_rp + jb * ld_rp + i]
   float* rowpart; long long s_rp; int ld_rp;

@@ -88,8 +88,11 @@ __device__ __forceinline__ float weight_step(float w, float x, float wscale, flo
 
 // Streaming (nontemporal) loads and stores, for data that a launch touches
 // once: the X state in the update and final epilogues and in NorMuon's
-// weight pass, the weights, and the gradient, momentum and X_0 of prep.  Kept out of the caches, they leave
-// L2 to the operand panels that the GEMM main loops re-read.
+// weight pass, the weights, and the gradient, momentum and X_0 of prep.
+// Kept out of the caches, they leave L2 to the operand panels that the GEMM
+// main loops re-read.  The UPDATE / FINAL and prep kernels take them (STRM)
+// for groups whose X state is larger than the last-level cache; smaller
+// groups keep X cached for the next launch.
 template <typename V>
 __device__ __forceinline__ V ld_nt(const V* p) { return __builtin_nontemporal_load(p); }
 template <typename V>
@@ -113,9 +116,11 @@ __device__ __forceinline__ void static_for(F&& f) {
 // layout are written directly, the others through a transposing LDS tile.
 //   CT = bf16: X_0 as its hi and lo planes (M x N);
 //   CT = fp32: X_0 (M x N) and X_0^T (N x M).
-template <typename GT, typename CT, bool MOM>
+template <typename GT, typename CT, bool MOM, bool STRM>
 __global__ __launch_bounds__(256) void prep_kernel(PrepLaunch launch) {
   const PrepArgs& a = launch.a;
+  auto ldx = [](const auto* q) { if constexpr (STRM) return ld_nt(q); else return *q; };
+  auto stx = [](auto v, auto* q) { if constexpr (STRM) st_nt(v, q); else *q = v; };
   __shared__ float tile[kPrepTile][kPrepTile + 1];
   __shared__ float red[4];
   constexpr bool HILO = sizeof(CT) == 2;
@@ -152,8 +157,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepLaunch launch) {
     if constexpr (HILO) {
       bf16_t hi, lo;
       split_bf16(u, hi, lo);
-      st_nt(hi, Xh + o);
-      st_nt(lo, Xl + o);
+      stx(hi, Xh + o);
+      stx(lo, Xl + o);
     } else {
       Xf[o] = u;
     }
@@ -168,10 +173,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepLaunch launch) {
     float u = 0.f;
     if (r < rows && c < cols) {
       const long long idx = (long long)r * cols + c;
-      const float gv = to_f32(ld_nt(g + idx));
+      const float gv = to_f32(ldx(g + idx));
       if constexpr (MOM) {
-        const float nb = a.mu * ld_nt(buf + idx) + gv;  // buf' = mu*buf + g
-        st_nt(nb, buf + idx);
+        const float nb = a.mu * ldx(buf + idx) + gv;  // buf' = mu*buf + g
+        stx(nb, buf + idx);
         u = gv + a.mu * nb;                     // u = g + mu*buf'
       } else {
         u = gv;
@@ -391,9 +396,13 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const void* p) {
 // (the mirrored triangle of A and B, the fp32 path's X^T, the weights of a
 // tall matrix) are staged in LDS as [j][i] rows and stored as coalesced
 // 16-byte chunks.
-template <typename T, int EPI, int BM, int BN, int WGM, int WGN, int S, bool QROW, bool BUFLD>
+template <typename T, int EPI, int BM, int BN, int WGM, int WGN, int S, bool QROW, bool BUFLD,
+          bool STRM>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch) {
   const GemmArgs& a = launch.a;
+  // STRM: the X state and the weights are streamed (see ld_nt)
+  auto ldx = [](const auto* q) { if constexpr (STRM) return ld_nt(q); else return *q; };
+  auto stx = [](auto v, auto* q) { if constexpr (STRM) st_nt(v, q); else *q = v; };
   constexpr bool SCHED = S == 2;
   constexpr int NT = 64 * WGM * WGN, NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
@@ -728,7 +737,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
           float ein[16];
           static_for<16>([&](auto r) {
             const long long o = (long long)(ib + 8 * (r / 4) + (r % 4)) * a.ldx + j;
-            if constexpr (HILO) ein[r] = to_f32(ld_nt(Xh + o)) + to_f32(ld_nt(Xl + o));
+            if constexpr (HILO) ein[r] = to_f32(ldx(Xh + o)) + to_f32(ldx(Xl + o));
             else ein[r] = Xf[o];
           });
           const int jl = jl0 + ni * 32;
@@ -766,7 +775,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
 #pragma unroll
             for (int s = 0; s < HALF; ++s) {
               if (a.vec_tall && nval[s] == 4) {
-                wv[s] = ld_nt(reinterpret_cast<const f32x4_t*>(W + off[s]));
+                wv[s] = ldx(reinterpret_cast<const f32x4_t*>(W + off[s]));
               } else {
 #pragma unroll
                 for (int t = 0; t < 4; ++t) wv[s][t] = t < nval[s] ? W[off[s] + t] : 0.f;
@@ -779,7 +788,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
               for (int t = 0; t < 4; ++t)
               w[t] = weight_step(wv[s][t], xv[s][t], wscale, a.neg_lrwd, a.cautious);
               if (a.vec_tall && nval[s] == 4) {
-                st_nt(w, reinterpret_cast<f32x4_t*>(W + off[s]));
+                stx(w, reinterpret_cast<f32x4_t*>(W + off[s]));
               } else {
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
@@ -854,8 +863,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
     auto load = [&](auto mi, auto b) __attribute__((always_inline)) {
       static_for<RUNS>([&](auto s) {
         const long long o = offset(decltype(mi)::value, s);
-        hv[decltype(b)::value][s] = ld_nt(reinterpret_cast<const u32x4_t*>(Xh + o));
-        lv[decltype(b)::value][s] = ld_nt(reinterpret_cast<const u32x4_t*>(Xl + o));
+        hv[decltype(b)::value][s] = ldx(reinterpret_cast<const u32x4_t*>(Xh + o));
+        lv[decltype(b)::value][s] = ldx(reinterpret_cast<const u32x4_t*>(Xl + o));
       });
     };
     load(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
@@ -878,8 +887,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
           const int i = i_base + mi * 32 + rr0 + RSTEP * s, j = j_base + cc;
           const float* Wr = W + (long long)i * a.n + j;
           if (i < a.m && a.vec_wide && j + 8 <= a.n) {
-            wv[s][0] = ld_nt(reinterpret_cast<const f32x4_t*>(Wr));
-            wv[s][1] = ld_nt(reinterpret_cast<const f32x4_t*>(Wr + 4));
+            wv[s][0] = ldx(reinterpret_cast<const f32x4_t*>(Wr));
+            wv[s][1] = ldx(reinterpret_cast<const f32x4_t*>(Wr + 4));
           } else {
             static_for<8>([&](auto e) {
               wv[s][e / 4][e % 4] = i < a.m && j + e < a.n ? Wr[(int)e] : 0.f;
@@ -913,8 +922,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
                 w1[(int)t] = weight_step(wv[s][1][(int)t], x[4 + t], wscale, a.neg_lrwd, a.cautious);
               });
               if (full) {
-                st_nt(w0, reinterpret_cast<f32x4_t*>(Wr));
-                st_nt(w1, reinterpret_cast<f32x4_t*>(Wr + 4));
+                stx(w0, reinterpret_cast<f32x4_t*>(Wr));
+                stx(w1, reinterpret_cast<f32x4_t*>(Wr + 4));
               } else {
                 static_for<8>([&](auto e) {
                   if (j + e < a.n) Wr[(int)e] = e < 4 ? w0[e & 3] : w1[e & 3];
@@ -974,8 +983,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
         });
         const long long o = offset(mi, s);
         // lo is updated in place: only this block reads X[i][j]'s lo
-        st_nt(ho, reinterpret_cast<u32x4_t*>(Xh_next + o));
-        st_nt(lo, reinterpret_cast<u32x4_t*>(Xl + o));
+        stx(ho, reinterpret_cast<u32x4_t*>(Xh_next + o));
+        stx(lo, reinterpret_cast<u32x4_t*>(Xl + o));
         if constexpr (ROWS) {
           // the row's sum over the wave's 64 columns, from the 8 lanes of
           // its runs in a fixed butterfly order (all lanes are active here)
@@ -1243,8 +1252,13 @@ hipError_t launch_prep(int grad_bf16, int compute_bf16, int momentum, const Prep
                        const PrepTable& t, int batch, hipStream_t s) {
   const dim3 grid(a.nblk, batch), block(256);
   const PrepLaunch launch{a, t};
-#define MUON_PREP(GT, CT, MOM) \
-  hipLaunchKernelGGL((prep_kernel<GT, CT, MOM>), grid, block, 0, s, launch)
+#define MUON_PREP(GT, CT, MOM)                                                      \
+  do {                                                                              \
+    if (a.stream)                                                                   \
+      hipLaunchKernelGGL((prep_kernel<GT, CT, MOM, true>), grid, block, 0, s, launch);  \
+    else                                                                            \
+      hipLaunchKernelGGL((prep_kernel<GT, CT, MOM, false>), grid, block, 0, s, launch); \
+  } while (0)
   if (grad_bf16) {
     if (compute_bf16) {
       if (momentum) MUON_PREP(bf16_t, bf16_t, true); else MUON_PREP(bf16_t, bf16_t, false);
@@ -1324,25 +1338,33 @@ static void launch_gemm_t(int tile, const GemmArgs& a, const WeightTable& t, dim
     // `tile` rows of the leading dimension
     const long long ld = a.ldp > a.ldq ? a.ldp : a.ldq;
     const bool buf = buffer_loads(E) && (long long)tile * ld * (long long)sizeof(T) < (1LL << 31);
-    if (tile == 256) {
-      if (buf)
-        hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 2, QR, true>), grid, dim3(512), 0,
-                           s, launch);
-      else
-        hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 2, QR, false>), grid, dim3(512), 0,
-                           s, launch);
-    } else {
-      if (buf)
-        hipLaunchKernelGGL((gemm_kernel<T, E, 128, 128, 2, 2, 2, QR, true>), grid, dim3(256), 0,
-                           s, launch);
-      else
-        hipLaunchKernelGGL((gemm_kernel<T, E, 128, 128, 2, 2, 2, QR, false>), grid, dim3(256), 0,
-                           s, launch);
-    }
+    auto go = [&](auto strm) {
+      constexpr bool ST = decltype(strm)::value;
+      if (tile == 256) {
+        if (buf)
+          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 2, QR, true, ST>), grid,
+                             dim3(512), 0, s, launch);
+        else
+          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 2, QR, false, ST>), grid,
+                             dim3(512), 0, s, launch);
+      } else {
+        if (buf)
+          hipLaunchKernelGGL((gemm_kernel<T, E, 128, 128, 2, 2, 2, QR, true, ST>), grid,
+                             dim3(256), 0, s, launch);
+        else
+          hipLaunchKernelGGL((gemm_kernel<T, E, 128, 128, 2, 2, 2, QR, false, ST>), grid,
+                             dim3(256), 0, s, launch);
+      }
+    };
+    // streaming accesses exist only in the row-major-X (UPDATE / FINAL) epilogues
+    if (QR && a.stream)
+      go(std::integral_constant<bool, QR>{});
+    else
+      go(std::false_type{});
     return;
   }
-  hipLaunchKernelGGL((gemm_kernel<T, E, 128, 128, 2, 2, 0, QR, false>), grid, dim3(256), 0, s,
-                     launch);
+  hipLaunchKernelGGL((gemm_kernel<T, E, 128, 128, 2, 2, 0, QR, false, false>), grid, dim3(256),
+                     0, s, launch);
 }
 
 hipError_t launch_gemm(int compute_bf16, int epi, int tile, const GemmArgs& a_in,
