@@ -44,8 +44,8 @@ int tile_pref() {
 int group_m() {
   static const int v = [] {
     const char* e = std::getenv("MUON_GROUP_M");
-    const int g = e ? std::atoi(e) : 4;
-    return g >= 1 ? g : 4;
+    const int g = e ? std::atoi(e) : 8;
+    return g >= 1 ? g : 8;
   }();
   return v;
 }
