@@ -50,6 +50,16 @@ int group_m() {
   return v;
 }
 
+// MUON_STREAM=0|1 forces the cached or the streaming kernel variants for
+// every chunk (a testing and tuning knob; see kStreamBytes).
+int stream_pref() {
+  static const int v = [] {
+    const char* e = std::getenv("MUON_STREAM");
+    return e ? (std::atoi(e) != 0 ? 1 : 0) : -1;
+  }();
+  return v;
+}
+
 // 256 x 256 tiles unless that leaves fewer than two blocks per CU.
 int pick_tile(bool cbf16, long long tiles_at_256, int batch) {
   const int pref = tile_pref();
@@ -218,7 +228,8 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
   const double pmn = cnt * (double)MN, pmm = cnt * (double)MM;  // padded elements
 
   // X state: hi twice + lo (bf16), or X + X^T twice (fp32)
-  const bool stream = pmn * (cbf16 ? 6.0 : 12.0) > kStreamBytes;
+  const bool stream =
+      stream_pref() >= 0 ? stream_pref() == 1 : pmn * (cbf16 ? 6.0 : 12.0) > kStreamBytes;
   PrepArgs pa{};
   pa.m = L.m; pa.n = L.n; pa.M = L.M; pa.N = L.N;
   pa.stream = stream;
