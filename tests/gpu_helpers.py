@@ -7,12 +7,14 @@ import numpy as np
 BF16_TOL = 2e-2   # relative Frobenius error, bf16 MFMA path
 FP32_TOL = 1e-4   # relative Frobenius error, fp32 path
 BUF_TOL = 1e-6    # momentum buffer, fp32 arithmetic vs fp64
-# bf16 path on matrices with min(rows, cols) < 64: the rounding of a few
-# bf16 operands does not average out.  Emulating the bf16 design (bf16 X, A,
-# B operands, fp32 accumulation and fp32 X) on 200 Gaussian draws per shape
-# gives median ~2e-2 and maxima 3e-2 (16x8), 4.5e-2 (5x5), 8.6e-2 (8x2);
-# from min dim 128 on the spread collapses to 1.5e-2 +- 5e-4.
-BF16_SMALL_TOL = 1.5e-1
+# bf16 path on matrices with min(rows, cols) < 64: the rounding of a few bf16
+# operands does not average out, and the error spreads well past 2e-2.  One
+# bound per oriented shape (m, n) the GPU tests use, each between the maximum
+# over 1000 Gaussian draws of the emulated bf16 path and 1.25 times it
+# (tests/test_bf16_emulation.py recomputes the maxima and checks every entry:
+# 1x1 0.120, 1x5 0.094, 2x8 0.117, 5x5 0.072, 8x16 0.039).  From min dim 64 on
+# the emulated maximum stays below 2e-2 (64x64: 1.8e-2, 128x128: 1.5e-2).
+BF16_SMALL_TOL = {(1, 1): 0.15, (1, 5): 0.11, (2, 8): 0.14, (5, 5): 0.09, (8, 16): 0.048}
 SMALL_DIM = 64
 
 
@@ -20,7 +22,10 @@ def tol(compute, shape=None):
     if compute != "bf16":
         return FP32_TOL
     if shape is not None and min(shape) < SMALL_DIM:
-        return BF16_SMALL_TOL
+        key = (min(shape), max(shape))
+        if key not in BF16_SMALL_TOL:
+            raise KeyError(f"no derived bf16 bound for the small shape {key}")
+        return BF16_SMALL_TOL[key]
     return BF16_TOL
 
 

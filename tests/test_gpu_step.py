@@ -158,3 +158,43 @@ def test_refuses_tensors_off_the_device():
     with pytest.raises(ValueError):
         mn.orthogonalize(g, out=torch.empty(8, 16))
     assert torch.count_nonzero(p) == 0 and torch.count_nonzero(b) == 0
+
+
+def test_non_finite_values_propagate_like_the_oracle():
+    """One NaN gradient element and one infinite weight, in two different
+    matrices of one call: NaN exactly where the oracle has NaN (the momentum
+    at that element, all of that matrix's new weights), the infinite weight
+    stays infinite and leaves the rest of its matrix bitwise as in a clean
+    run (its direction does not depend on W), and the third matrix is
+    bitwise unchanged by the others' non-finite values."""
+    announce("non-finite propagation")
+    w = dataclasses.replace(wl.GPT_D768, shapes=((96, 256), (256, 96), (128, 128)))
+    clean = wl.make_inputs(w, device=DEV)
+    dirty = {k: ([t.clone() for t in v] if k in ("params", "grads", "bufs") else v)
+             for k, v in clean.items()}
+    dirty["grads"][0][5, 7] = float("nan")
+    dirty["params"][1][3, 2] = float("inf")
+    ref_in = {k: [to64(t) for t in dirty[k]] for k in ("params", "grads", "bufs")}
+    for inp in (clean, dirty):
+        mn.step(inp["params"], inp["grads"], inp["bufs"], mu=w.mu, lr=w.lr,
+                scales=inp["scales"], coeffs=w.coeff_table, compute="bf16")
+    torch.cuda.synchronize()
+    for k in range(3):
+        new_w, new_buf, _ = oracle.muon_step(ref_in["params"][k], ref_in["grads"][k],
+                                             ref_in["bufs"][k], w.mu, w.lr, dirty["scales"][k],
+                                             w.coeff_table)
+        got_w, got_buf = to64(dirty["params"][k]), to64(dirty["bufs"][k])
+        assert np.array_equal(np.isnan(got_w), np.isnan(new_w)), k
+        assert np.array_equal(np.isnan(got_buf), np.isnan(new_buf)), k
+        assert np.array_equal(np.isinf(got_w), np.isinf(new_w)), k
+    assert torch.isnan(dirty["params"][0]).all()
+    assert torch.isnan(dirty["bufs"][0]).sum() == 1
+    keep = torch.ones_like(dirty["bufs"][0], dtype=torch.bool)
+    keep[5, 7] = False
+    assert torch.equal(dirty["bufs"][0][keep], clean["bufs"][0][keep])
+    assert dirty["params"][1][3, 2] == float("inf")
+    keep = torch.ones_like(dirty["params"][1], dtype=torch.bool)
+    keep[3, 2] = False
+    assert torch.equal(dirty["params"][1][keep], clean["params"][1][keep])
+    assert torch.equal(dirty["params"][2], clean["params"][2])
+    assert torch.equal(dirty["bufs"][2], clean["bufs"][2])

@@ -3,11 +3,13 @@ decay and NorMuon scaling on top of the plain step, mixed shapes (tall,
 wide, square, ragged), both compute precisions, and the second-moment
 moving average carried over two steps.
 
-The cautious mask is a sign decision on O'*W.  Where |O'| lies within the
-arithmetic's error of zero both decisions are correct; there the comparison
-takes the oracle's value for whichever decision the GPU made, and the
-magnitude part (-lr*scale*O') is still compared.  Everywhere else the mask
-must agree."""
+The cautious mask is a sign decision on O'*W.  The GPU's own direction O'
+is read from a twin call without decay on copies of the same state (the
+same kernels, so the same O'); where it and the oracle's O' differ in sign
+(|O'_ref| within the GPU's measured error of that element) both decisions
+are correct, and the comparison takes the oracle's value for whichever
+decision the GPU made; the magnitude part (-lr*scale*O') is still compared.
+Everywhere else the mask must agree with the oracle's."""
 import dataclasses
 
 import numpy as np
@@ -25,9 +27,10 @@ SHAPES = ((64, 128), (128, 64), (100, 300), (300, 100), (64, 64), (1, 5), (5, 1)
           (257, 129), (64, 128), (256, 768), (768, 256))
 
 
-def expected_dw(ref, w_before, dw_gpu, lr, scale, wd, cautious, margin):
-    """Oracle dW with the cautious mask taken from the GPU where |O'| is below
-    ``margin`` (both decisions valid there)."""
+def expected_dw(ref, w_before, dw_gpu, lr, scale, wd, cautious, o_gpu):
+    """Oracle dW, with the cautious mask taken from the GPU where the GPU's
+    direction o_gpu and the oracle's differ in sign (both decisions are
+    correct there); the fp32 rounding of the recovered o_gpu is allowed for."""
     o, w = ref["o"], w_before
     dw_keep = -lr * scale * o
     dw_decay = dw_keep - lr * wd * w
@@ -35,9 +38,26 @@ def expected_dw(ref, w_before, dw_gpu, lr, scale, wd, cautious, margin):
         return dw_decay
     mask = o * w >= 0
     dw = np.where(mask, dw_decay, dw_keep)
-    amb = np.abs(o) <= margin
+    slack = 4.0 * np.spacing(np.abs(w).astype(np.float32)) / (lr * scale)
+    amb = np.abs(o) <= np.abs(o_gpu - o) + slack
     closer = np.where(np.abs(dw_gpu - dw_decay) <= np.abs(dw_gpu - dw_keep), dw_decay, dw_keep)
     return np.where(amb, closer, dw)
+
+
+def gpu_direction(w, inp, vs, indices, **call):
+    """The update direction O' the GPU applies, for matrices ``indices``: the
+    same step_ex call without weight decay on copies of the weights,
+    momentum and second moments, read back from its weight change."""
+    params = [p.clone() for p in inp["params"]]
+    bufs = [b.clone() for b in inp["bufs"]]
+    vv = [v.clone() for v in vs] if vs is not None else None
+    before = {k: to64(params[k]) for k in indices}
+    mn.step_ex(params, inp["grads"], bufs, mu=w.mu, lr=w.lr, scales=inp["scales"],
+               coeffs=w.coeff_table, second_moments=vv, **{**call, "weight_decay": 0.0})
+    torch.cuda.synchronize()
+    out = {k: (to64(params[k]) - before[k]) / (-w.lr * inp["scales"][k]) for k in indices}
+    del params, bufs, vv
+    return out
 
 
 def run_case(compute, wd, cautious, normuon, steps=1, shapes=SHAPES, beta2=0.9,
@@ -50,11 +70,13 @@ def run_case(compute, wd, cautious, normuon, steps=1, shapes=SHAPES, beta2=0.9,
                   v=to64(vs[k]) if normuon else None) for k in range(len(shapes))]
     for step in range(steps):
         before = [to64(p) for p in inp["params"]]
+        call = dict(compute=compute, cautious=cautious, beta2=beta2 if normuon else None,
+                    normuon_eps=normuon_eps if normuon else None)
+        o_gpu = (gpu_direction(w, inp, vs, range(len(shapes)), **call)
+                 if cautious and wd > 0 else {})
         mn.step_ex(inp["params"], inp["grads"], inp["bufs"], mu=w.mu, lr=w.lr,
-                   scales=inp["scales"], coeffs=w.coeff_table, compute=compute,
-                   weight_decay=wd, cautious=cautious, second_moments=vs,
-                   beta2=beta2 if normuon else None,
-                   normuon_eps=normuon_eps if normuon else None)
+                   scales=inp["scales"], coeffs=w.coeff_table, second_moments=vs,
+                   weight_decay=wd, **call)
         torch.cuda.synchronize()
         for k, shape in enumerate(shapes):
             g = to64(inp["grads"][k])
@@ -65,9 +87,8 @@ def run_case(compute, wd, cautious, normuon, steps=1, shapes=SHAPES, beta2=0.9,
                                       beta2=beta2, normuon_eps=normuon_eps)
             t = tol(compute, shape)
             dw_gpu = to64(inp["params"][k]) - before[k]
-            rms = float(np.sqrt(np.mean(ref["o"] ** 2)))
             dw_ref = expected_dw(ref, before[k], dw_gpu, w.lr, inp["scales"][k], wd, cautious,
-                                 margin=8 * t * rms)
+                                 o_gpu.get(k))
             err = oracle.relative_frobenius_error(dw_gpu, dw_ref)
             assert err <= t, (step, shape, err)
             assert oracle.relative_frobenius_error(to64(inp["bufs"][k]), ref["buf"]) <= BUF_TOL
@@ -127,22 +148,28 @@ def test_gpt_3p8b_step_ex_sampled():
     bufs = {k: to64(inp["bufs"][k]) for k in samples}
     v0 = {k: to64(vs[k]) for k in samples}
     opt = dict(weight_decay=0.1, cautious=True, beta2=0.95, normuon_eps=1e-8)
+    o_gpu = gpu_direction(w, inp, vs, samples, compute="bf16", cautious=True, beta2=0.95,
+                          normuon_eps=1e-8)
     mn.step_ex(inp["params"], inp["grads"], inp["bufs"], mu=w.mu, lr=w.lr,
                scales=inp["scales"], coeffs=w.coeff_table, compute="bf16",
                second_moments=vs, **opt)
     torch.cuda.synchronize()
+    amb_frac = []
     for k in samples:
         print("  oracle matrix", k, w.shapes[k], flush=True)
         ref = oracle.muon_step_ex(before[k], to64(inp["grads"][k]), bufs[k], w.mu, w.lr,
                                   inp["scales"][k], w.coeff_table, second_moment=v0[k], **opt)
         t = tol("bf16", w.shapes[k])
         dw_gpu = to64(inp["params"][k]) - before[k]
-        rms = float(np.sqrt(np.mean(ref["o"] ** 2)))
         dw_ref = expected_dw(ref, before[k], dw_gpu, w.lr, inp["scales"][k], 0.1, True,
-                             margin=8 * t * rms)
+                             o_gpu[k])
+        amb_frac.append(float(np.mean(np.abs(ref["o"]) <= np.abs(o_gpu[k] - ref["o"]))))
         assert oracle.relative_frobenius_error(dw_gpu, dw_ref) <= t, k
         assert oracle.relative_frobenius_error(to64(inp["bufs"][k]), ref["buf"]) <= BUF_TOL
         assert oracle.relative_frobenius_error(to64(vs[k]), ref["v"]) <= 2 * t
+    # the sign of O' is in doubt (either mask decision valid) for few elements
+    print("  elements with either mask decision valid:", amb_frac, flush=True)
+    assert max(amb_frac) <= 0.02
 
 
 @pytest.mark.parametrize("compute", ["bf16", "fp32"])

@@ -388,3 +388,120 @@ def test_planted_normalisation_mistake_is_caught(monkeypatch):
     g = rng(22).standard_normal((16, 8))
     o = mo.orthogonalize(g, QUINTIC)
     assert np.max(np.abs(o - spectral_closed_form(g, QUINTIC))) > 1e-3
+
+
+# ------------------------------ the comparison every parity verdict rests on
+def _rfe_pins(rfe):
+    """True if ``rfe`` passes every hand-computed case of the relative
+    Frobenius error ||y - y_ref||_F / ||y_ref||_F."""
+    cases = [
+        # diff (3, -1): sqrt(10) / ||(0, 5)|| = sqrt(10) / 5
+        ([[3.0, 4.0]], [[0.0, 5.0]], math.sqrt(10.0) / 5.0),
+        # diff (0, 0, 0, 4): 4 / ||ref|| = 4 / 3, where ||y|| = 5 and the
+        # largest entries are 4 (diff) and 2 (ref)
+        ([[1.0, 2.0], [2.0, 4.0]], [[1.0, 2.0], [2.0, 0.0]], 4.0 / 3.0),
+        # an error of 0.14, whose square (0.0196) would pass a 2e-2 bar
+        ([[1.0, 0.14]], [[1.0, 0.0]], 0.14),
+        # many small errors: ||(0.1, ..., 0.1)|| over 100 entries = 1, ref norm 10
+        (np.full((10, 10), 1.1), np.ones((10, 10)), 0.1),
+        # both zero: no error; a zero reference with a non-zero result: infinite
+        ([[0.0, 0.0]], [[0.0, 0.0]], 0.0),
+        ([[1e-30, 0.0]], [[0.0, 0.0]], float("inf")),
+    ]
+    for y, ref, want in cases:
+        got = rfe(y, ref)
+        if math.isinf(want):
+            if not math.isinf(got):
+                return False
+        elif abs(got - want) > 1e-12 * max(1.0, want):
+            return False
+    return True
+
+
+def test_relative_frobenius_error_hand_computed():
+    assert _rfe_pins(oracle.relative_frobenius_error)
+
+
+def _rfe_slips():
+    def squared_ratio(y, ref):
+        y, ref = np.asarray(y, float), np.asarray(ref, float)
+        d = float(np.sum(ref * ref))
+        return 0.0 if d == 0 else float(np.sum((y - ref) ** 2)) / d
+
+    def result_in_denominator(y, ref):
+        y, ref = np.asarray(y, float), np.asarray(ref, float)
+        d = float(np.linalg.norm(y))
+        return 0.0 if d == 0 else float(np.linalg.norm(y - ref)) / d
+
+    def max_abs(y, ref):
+        y, ref = np.asarray(y, float), np.asarray(ref, float)
+        d = float(np.max(np.abs(ref)))
+        return 0.0 if d == 0 else float(np.max(np.abs(y - ref))) / d
+
+    def absolute(y, ref):
+        return float(np.linalg.norm(np.asarray(y, float) - np.asarray(ref, float)))
+
+    return [squared_ratio, result_in_denominator, max_abs, absolute]
+
+
+@pytest.mark.parametrize("slip", _rfe_slips(), ids=lambda f: f.__name__)
+def test_relative_frobenius_error_slips_fail_the_pins(slip):
+    assert not _rfe_pins(slip)
+
+
+# -------------------- the closed form the full-size GPU tests compare with
+def test_gram_closed_form_matches_the_oracle():
+    """tests/gpu_helpers.gram_closed_form computes U phi(S) V^T from the
+    eigendecomposition of X X^T (so it runs at any size); on small cases it
+    must equal the step-by-step oracle, for the quintic and the 30-step cubic
+    on ill-conditioned inputs, rank-deficient ones and per-step tables."""
+    from gpu_helpers import gram_closed_form, normalise
+    cases = [
+        (rng(40).standard_normal((48, 160)), QUINTIC, 1e-10),
+        (with_spectrum(64, 256, 1e-4, 1.0, 41), QUINTIC, 1e-10),
+        (with_spectrum(64, 256, 1e-4, 1.0, 42), [wl.CUBIC] * 30, 1e-8),
+        (rng(43).standard_normal((32, 8)) @ rng(44).standard_normal((8, 96)), QUINTIC, 1e-10),
+        (rng(45).standard_normal((40, 120)), [wl.QUINTIC, wl.CUBIC] * 3, 1e-10),
+    ]
+    for g, coeffs, bound in cases:
+        ref = oracle.orthogonalize(g, coeffs)
+        cf = gram_closed_form(normalise(g), coeffs)
+        assert oracle.relative_frobenius_error(cf, ref) <= bound
+
+
+def test_gram_closed_form_planted_mistake_fails():
+    # taking phi(l) instead of phi(sqrt l) / sqrt l would be a plausible slip
+    from gpu_helpers import gram_eig, normalise
+    g = rng(46).standard_normal((24, 80))
+    x0 = normalise(g)
+    lam, v = gram_eig(x0)
+    s = np.sqrt(np.maximum(lam, 0.0))
+    wrong = (v * np.array([scalar_map(x, QUINTIC) for x in s])) @ (v.T @ x0)
+    ref = oracle.orthogonalize(g, QUINTIC)
+    assert oracle.relative_frobenius_error(wrong, ref) > 0.5
+
+
+# --------------------------------------------------- non-finite values
+def test_nan_gradient_element_propagates():
+    """One NaN in a gradient: the momentum is NaN at that element only, and
+    the normalisation spreads it to every element of O and of the new
+    weights (the header's promise: non-finite values propagate)."""
+    g = rng(47).standard_normal((6, 10))
+    g[2, 3] = np.nan
+    buf = rng(48).standard_normal((6, 10)) * 1e-3
+    w = rng(49).standard_normal((6, 10)) * 0.02
+    new_w, new_buf, o = oracle.muon_step(w, g, buf, 0.95, 0.02, 1.0, QUINTIC)
+    assert np.isnan(new_buf[2, 3]) and np.isfinite(np.delete(new_buf.ravel(), 2 * 10 + 3)).all()
+    assert np.isnan(o).all() and np.isnan(new_w).all()
+
+
+def test_infinite_weight_element_stays_local():
+    """An infinite weight does not enter the direction: only its own element
+    of the new weights is non-finite."""
+    g = rng(50).standard_normal((6, 10))
+    w = rng(51).standard_normal((6, 10)) * 0.02
+    w[4, 1] = np.inf
+    new_w, _, o = oracle.muon_step(w, g, np.zeros_like(g), 0.95, 0.02, 1.0, QUINTIC)
+    assert np.isfinite(o).all()
+    assert new_w[4, 1] == np.inf
+    assert np.isfinite(np.delete(new_w.ravel(), 4 * 10 + 1)).all()
