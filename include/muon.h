@@ -90,8 +90,8 @@ int muon_plan_groups(int n, const int* rows, const int* cols, int* group_of,
  * matrices (page 1, Newton-Schulz paragraph), and writes out = X_{n_steps}.
  *   in, out       device, `batch` matrices rows x cols, matrix i at
  *                 element offset i * batch_stride (batch_stride >= rows*cols);
- *                 out may alias in exactly (same pointer); any other overlap
- *                 is undefined.
+ *                 out may alias in exactly (same pointer and same dtype); any
+ *                 other overlap returns MUON_ERR_INVALID_ARG.
  *   in_dtype      MUON_BF16 or MUON_FP32; out_dtype likewise.
  *   coeffs        host, n_steps rows (copied during the call).
  *   eps           >= 0, finite (the step's default is 1e-7).
@@ -206,8 +206,13 @@ typedef struct {
   int batch;       /* matrices in the launch */
   int step;        /* Newton-Schulz step, -1 for PREP and NORM */
   float ms;        /* elapsed time between HIP events around the launch */
-  double flops;    /* counted flops: GRAM 2m^2n, POLY 2m^3, UPDATE/FINAL 2m^2n per matrix */
-  double bytes;    /* algorithmic HBM bytes of the launch (see the design notes) */
+  double flops;    /* counted flops: GRAM 2m^2n, POLY 2m^3, UPDATE/FINAL 2m^2n per matrix
+                      (GRAMQ: m^2n per launch, the Gram's count split over its two) */
+  double bytes;    /* algorithmic HBM bytes of the launch: each operand, input
+                      and output of the launch read or written once */
+  double exec_flops; /* flops the launch's MFMAs execute: its tiles over the
+                        padded shape (lower-triangle tiles for GRAM, POLY and
+                        GRAMQ) */
 } muon_timing_record;
 
 /* Turn per-launch HIP-event timing on (1) or off (0) for later calls in
@@ -219,6 +224,22 @@ int muon_timing_enable(int on);
  * to `out`, set *n_out to the number written, and clear the log.
  * Returns MUON_OK or MUON_ERR_HIP. */
 int muon_timing_read(muon_timing_record* out, int cap, int* n_out);
+
+/* Probes of what the chip sustains, timed by the caller next to the step
+ * (HIP events on `stream`, around the one kernel each call enqueues).  Not
+ * part of the Muon step; they compute nothing of it.
+ *   muon_probe_mfma_bf16  `blocks` workgroups of 8 waves, each wave running
+ *       `iters` rounds of 4 independent v_mfma_f32_32x32x16_bf16 on register
+ *       operands, no memory traffic: the launch performs exactly
+ *       blocks * 8 * iters * 4 * 32768 flops.  `sink` is device memory of
+ *       blocks * 512 floats (overwritten; the values mean nothing).
+ *   muon_probe_copy  copies `bytes` (a multiple of 16; src and dst device
+ *       pointers, 16-byte aligned, not overlapping) in 16-byte accesses with
+ *       `blocks` workgroups of 256 threads: 2 * bytes of HBM traffic.
+ * Both return MUON_ERR_INVALID_ARG for bad arguments (nothing enqueued) and
+ * MUON_ERR_HIP if the launch fails. */
+int muon_probe_mfma_bf16(int blocks, int iters, float* sink, hipStream_t stream);
+int muon_probe_copy(const void* src, void* dst, size_t bytes, int blocks, hipStream_t stream);
 
 #ifdef __cplusplus
 }

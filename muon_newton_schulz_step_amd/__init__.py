@@ -77,7 +77,15 @@ def _coeffs(coeffs, n_steps=None):
 
 
 class Workspace:
-    """A reusable device buffer; grows to the largest request seen."""
+    """A reusable device buffer; grows to the largest request seen.
+
+    The library's kernels read and write it as they run, so one Workspace
+    must not serve two calls that can run at the same time (two streams):
+    their kernels would share scratch.  Calls on one stream are ordered and
+    may share it.  When it is used on a stream other than the one it was
+    allocated on, the buffer is marked as in use there, so that PyTorch's
+    caching allocator does not hand its memory out again (after it grows)
+    before that stream's work is done."""
 
     def __init__(self, device=None):
         self.device = device
@@ -88,9 +96,15 @@ class Workspace:
         if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
             self.buf = None
             self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+            self._stream = torch.cuda.current_stream(device)
+        cur = torch.cuda.current_stream(device)
+        if cur != self._stream:
+            self.buf.record_stream(cur)
         return self.buf
 
 
+# Default workspaces, one per (device, stream): calls on different streams
+# never share scratch.
 _default_ws: dict = {}
 
 
@@ -107,7 +121,8 @@ def _check_device(device, **tensors):
 
 def _workspace(nbytes: int, device, workspace):
     if workspace is None:
-        workspace = _default_ws.setdefault(str(device), Workspace())
+        key = (str(device), _torch().cuda.current_stream(device).cuda_stream)
+        workspace = _default_ws.setdefault(key, Workspace())
     if isinstance(workspace, Workspace):
         buf = workspace.get(nbytes, device)
         return buf.data_ptr(), buf.numel()
@@ -263,6 +278,29 @@ def _step(params, grads, bufs, second_moments, opt, *, mu, lr, scales, coeffs, n
         raise MuonError(st, where)
 
 
+def probe_mfma_bf16(sink, blocks: int, iters: int) -> float:
+    """Enqueue the MFMA rate probe on the current stream; returns the flops the
+    launch performs (time it with events on the same stream)."""
+    st = lib().muon_probe_mfma_bf16(blocks, iters, ctypes.c_void_p(sink.data_ptr()),
+                                    _stream(sink.device))
+    if st != MUON_OK:
+        raise MuonError(st, "muon_probe_mfma_bf16")
+    return float(blocks) * 8 * iters * 4 * 32768
+
+
+def probe_copy(src, dst, blocks: int) -> float:
+    """Enqueue the plain copy probe src -> dst (same size, bytes a multiple of
+    16) on the current stream; returns the HBM bytes it moves (read + write)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must have the same size")
+    st = lib().muon_probe_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                               nbytes, blocks, _stream(src.device))
+    if st != MUON_OK:
+        raise MuonError(st, "muon_probe_copy")
+    return 2.0 * nbytes
+
+
 def timing_enable(on: bool = True) -> bool:
     return bool(lib().muon_timing_enable(1 if on else 0))
 
@@ -275,4 +313,5 @@ def timing_read(cap: int = 1 << 16):
     if st != MUON_OK:
         raise MuonError(st, "muon_timing_read")
     return [dict(kind=KERNEL_KINDS[r.kind], m=r.m, n=r.n, batch=r.batch, step=r.step,
-                 ms=r.ms, flops=r.flops, bytes=r.bytes) for r in arr[:n.value]]
+                 ms=r.ms, flops=r.flops, bytes=r.bytes, exec_flops=r.exec_flops)
+            for r in arr[:n.value]]

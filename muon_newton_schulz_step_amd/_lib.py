@@ -27,6 +27,8 @@ EXPORTS = (
     "muon_step_ex",
     "muon_timing_enable",
     "muon_timing_read",
+    "muon_probe_mfma_bf16",
+    "muon_probe_copy",
 )
 
 
@@ -43,7 +45,8 @@ class MuonOptions(ctypes.Structure):
 class MuonTimingRecord(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int), ("m", ctypes.c_int), ("n", ctypes.c_int),
                 ("batch", ctypes.c_int), ("step", ctypes.c_int), ("ms", ctypes.c_float),
-                ("flops", ctypes.c_double), ("bytes", ctypes.c_double)]
+                ("flops", ctypes.c_double), ("bytes", ctypes.c_double),
+                ("exec_flops", ctypes.c_double)]
 
 
 _c_int_p = ctypes.POINTER(ctypes.c_int)
@@ -92,6 +95,10 @@ def load() -> ctypes.CDLL:
         ctypes.POINTER(MuonCoeff), ctypes.c_int, ctypes.c_float, ctypes.c_int,
         ctypes.POINTER(MuonOptions), _vp, ctypes.c_size_t, _vp]
     lib.muon_step_ex.restype = ctypes.c_int
+    lib.muon_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, _vp, _vp]
+    lib.muon_probe_mfma_bf16.restype = ctypes.c_int
+    lib.muon_probe_copy.argtypes = [_vp, _vp, ctypes.c_size_t, ctypes.c_int, _vp]
+    lib.muon_probe_copy.restype = ctypes.c_int
     lib.muon_timing_enable.argtypes = [ctypes.c_int]
     lib.muon_timing_enable.restype = ctypes.c_int
     lib.muon_timing_read.argtypes = [ctypes.POINTER(MuonTimingRecord), ctypes.c_int, _c_int_p]

@@ -167,8 +167,8 @@ struct Pending {
 std::vector<Pending> g_log;
 
 template <class F>
-hipError_t timed(int kind, int m, int n, int batch, int step, double flops, double bytes,
-                 hipStream_t s, F&& launch) {
+hipError_t timed(int kind, int m, int n, int batch, int step, double flops, double exec_flops,
+                 double bytes, hipStream_t s, F&& launch) {
   if (!g_timing.load(std::memory_order_relaxed)) return launch();
   hipEvent_t e0 = nullptr, e1 = nullptr;
   hipError_t err = hipEventCreate(&e0);
@@ -182,7 +182,7 @@ hipError_t timed(int kind, int m, int n, int batch, int step, double flops, doub
   err = launch();
   const hipError_t err2 = hipEventRecord(e1, s);
   if (err == hipSuccess) err = err2;
-  muon_timing_record r{kind, m, n, batch, step, 0.f, flops, bytes};
+  muon_timing_record r{kind, m, n, batch, step, 0.f, flops, bytes, exec_flops};
   std::lock_guard<std::mutex> lk(g_log_mu);
   g_log.push_back(Pending{r, e0, e1});
   return err;
@@ -247,17 +247,23 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
   // reads g (and momentum r/w); writes X_0: hi + lo, or X + X^T
   const double gsz = c.in_bf16 ? 2 : 4;
   const double prep_bytes = elems * (gsz + (c.momentum ? 8.0 : 0.0)) + pmn * (cbf16 ? 4.0 : 8.0);
-  hipError_t err = timed(MUON_K_PREP, L.m, L.n, c.cnt, -1, 0.0, prep_bytes, s, [&] {
+  hipError_t err = timed(MUON_K_PREP, L.m, L.n, c.cnt, -1, 0.0, 0.0, prep_bytes, s, [&] {
     return launch_prep(c.in_bf16, cbf16, c.momentum, pa, c.pt, c.cnt, s);
   });
   if (err != hipSuccess) return MUON_ERR_HIP;
-  err = timed(MUON_K_NORM, L.m, L.n, c.cnt, -1, 0.0, cnt * L.nblk * 4.0 + cnt * 4.0, s,
+  err = timed(MUON_K_NORM, L.m, L.n, c.cnt, -1, 0.0, 0.0, cnt * L.nblk * 4.0 + cnt * 4.0, s,
               [&] { return launch_norm(part, L.nblk, eps, inv, c.cnt, s); });
   if (err != hipSuccess) return MUON_ERR_HIP;
 
   const int t256 = L.M / 256;
   const int tile_sym = pick_tile(cbf16, (long long)t256 * (t256 + 1) / 2, c.cnt);
   const int tile_upd = pick_tile(cbf16, (long long)t256 * (L.N / 256), c.cnt);
+  // flops the MFMAs execute: lower-triangle tiles of M x M for the Gram and
+  // polynomial launches (K = N or M), all M x N for the update
+  const double tsym = L.M / tile_sym;
+  const double tri_el = tsym * (tsym + 1) / 2 * (double)tile_sym * tile_sym;
+  const double x_gram = 2.0 * tri_el * L.N * cnt, x_sym = 2.0 * tri_el * L.M * cnt;
+  const double x_upd = 2.0 * (double)L.M * L.N * L.M;  // per matrix
   for (int k = 0; k < n_steps; ++k) {
     const bool first = k == 0, last = k == n_steps - 1;
     const int cur = k & 1;
@@ -282,11 +288,11 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
       q.K = L.M; q.sP = q.sQ = MM; q.ldp = q.ldq = L.M;
       q.sC = MM; q.ldc = L.M; q.sAin = MM;
       q.P = B; q.Q = A; q.Ain = A; q.Alo = Alo; q.C = Tq;
-      err = timed(MUON_K_GRAMQ, L.m, L.n, c.cnt, k, cnt * m * m * n, 5.0 * pmm * es, s,
+      err = timed(MUON_K_GRAMQ, L.m, L.n, c.cnt, k, cnt * m * m * n, x_sym, 5.0 * pmm * es, s,
                   [&] { return launch_gemm(cbf16, EPI_POLY_LO, tile_sym, q, c.wt, c.cnt, s); });
       if (err != hipSuccess) return MUON_ERR_HIP;
       q.P = Tq; q.Q = B; q.Ain = Tq; q.Alo = nullptr; q.C = A;
-      err = timed(MUON_K_GRAMQ, L.m, L.n, c.cnt, k, cnt * m * m * n, 4.0 * pmm * es, s,
+      err = timed(MUON_K_GRAMQ, L.m, L.n, c.cnt, k, cnt * m * m * n, x_sym, 4.0 * pmm * es, s,
                   [&] { return launch_gemm(cbf16, EPI_POLY, tile_sym, q, c.wt, c.cnt, s); });
       if (err != hipSuccess) return MUON_ERR_HIP;
     } else {
@@ -297,7 +303,7 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
       g.sP = g.sQ = MN; g.ldp = g.ldq = L.N; g.K = L.N;
       g.C = A; g.sC = MM; g.ldc = L.M;
       g.Clo = L.qaq && qaq_step(k + 1, n_steps) ? Alo : nullptr;
-      err = timed(MUON_K_GRAM, L.m, L.n, c.cnt, k, cnt * 2.0 * m * m * n,
+      err = timed(MUON_K_GRAM, L.m, L.n, c.cnt, k, cnt * 2.0 * m * m * n, x_gram,
                   pmn * es + pmm * es * (g.Clo ? 1.5 : 1.0), s,
                   [&] {
                     return launch_gemm(cbf16, g.Clo ? EPI_GRAM_LO : EPI_GRAM, tile_sym, g, c.wt,
@@ -312,7 +318,7 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
     g.P = g.Q = A; g.sP = g.sQ = MM; g.ldp = g.ldq = L.M; g.K = L.M;
     g.C = B; g.sC = MM; g.ldc = L.M;
     g.Ain = A; g.sAin = MM;
-    err = timed(MUON_K_POLY, L.m, L.n, c.cnt, k, cnt * 2.0 * m * m * m, 3.0 * pmm * es, s,
+    err = timed(MUON_K_POLY, L.m, L.n, c.cnt, k, cnt * 2.0 * m * m * m, x_sym, 3.0 * pmm * es, s,
                 [&] { return launch_gemm(cbf16, EPI_POLY, tile_sym, g, c.wt, c.cnt, s); });
     if (err != hipSuccess) return MUON_ERR_HIP;
 
@@ -360,7 +366,8 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
       }
       const double upd_bytes = pmm * es + pmn * es + pmn * 4.0 + pmn * (cbf16 ? 4.0 : 8.0) +
                                (rows ? pmn / 16.0 : 0.0);
-      err = timed(MUON_K_UPDATE, L.m, L.n, c.cnt, k, cnt * 2.0 * m * m * n, upd_bytes, s, [&] {
+      err = timed(MUON_K_UPDATE, L.m, L.n, c.cnt, k, cnt * 2.0 * m * m * n, cnt * x_upd, upd_bytes,
+                  s, [&] {
         return launch_gemm(cbf16, rows ? EPI_UPDATE_ROWS : EPI_UPDATE, tile_upd, g, c.wt, c.cnt, s);
       });
     } else {
@@ -379,7 +386,7 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
         const double fin_bytes = bm * (double)MM * es + pmn_b * es + pmn_b * 4.0 +
                                  (c.final_mode == FINAL_WEIGHTS ? el_b * 8.0
                                                                 : el_b * (c.out_bf16 ? 2.0 : 4.0));
-        err = timed(MUON_K_FINAL, L.m, L.n, b, k, bm * 2.0 * m * m * n, fin_bytes, s,
+        err = timed(MUON_K_FINAL, L.m, L.n, b, k, bm * 2.0 * m * m * n, bm * x_upd, fin_bytes, s,
                     [&] { return launch_gemm(cbf16, epi, tile_upd, gf, c.wt, b, s); });
       }
     }
@@ -401,7 +408,7 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
     na.beta2 = c.beta2; na.eps2 = c.eps2;
     na.rinv = rinv;
     const double rows_read = L.rowsums ? pmn / 16.0 : pmn * 4.0;
-    err = timed(MUON_K_NORMUON, L.m, L.n, c.cnt, -1, 0.0, rows_read + cnt * L.m * 8.0, s,
+    err = timed(MUON_K_NORMUON, L.m, L.n, c.cnt, -1, 0.0, 0.0, rows_read + cnt * L.m * 8.0, s,
                 [&] { return launch_normuon_rows(cbf16, na, c.vt, c.cnt, s); });
     if (err != hipSuccess) return MUON_ERR_HIP;
     ApplyArgs aa{};
@@ -412,7 +419,7 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
     aa.Xh = Xh[n_steps & 1]; aa.Xl = Xl; aa.Xf = Xf;
     aa.rinv = rinv;
     aa.neg_lr = c.neg_lr; aa.neg_lrwd = c.neg_lrwd; aa.cautious = c.cautious;
-    err = timed(MUON_K_APPLY, L.m, L.n, c.cnt, -1, 0.0, elems * 12.0, s,
+    err = timed(MUON_K_APPLY, L.m, L.n, c.cnt, -1, 0.0, 0.0, elems * 12.0, s,
                 [&] { return launch_apply(cbf16, aa, c.wt, c.cnt, s); });
     if (err != hipSuccess) return MUON_ERR_HIP;
   }
@@ -644,7 +651,11 @@ int muon_orthogonalize(const void* in, int in_dtype, void* out, int out_dtype, i
   const size_t isz = in_dtype == MUON_BF16 ? 2 : 4, osz = out_dtype == MUON_BF16 ? 2 : 4;
   const size_t span_in = ((size_t)(batch - 1) * batch_stride + (size_t)rows * cols) * isz;
   const size_t span_out = ((size_t)(batch - 1) * batch_stride + (size_t)rows * cols) * osz;
-  if (in != out && overlap(in, span_in, out, span_out)) return MUON_ERR_INVALID_ARG;
+  // exact aliasing (same pointer, same dtype) is safe: each matrix's output
+  // lands where its own input was read, and every chunk reads its inputs
+  // before writing; anything else that overlaps is refused
+  const bool exact_alias = in == out && in_dtype == out_dtype;
+  if (!exact_alias && overlap(in, span_in, out, span_out)) return MUON_ERR_INVALID_ARG;
   if (overlap(workspace, need, in, span_in) || overlap(workspace, need, out, span_out))
     return MUON_ERR_INVALID_ARG;
 
@@ -689,6 +700,20 @@ int muon_step_ex(int n, const int* rows, const int* cols, void* const* params, i
   return step_impl(n, rows, cols, params, param_dtype, grads, grad_dtype, momentum,
                    second_moment, mu, lr, scale, coeffs, n_steps, eps, compute, options,
                    workspace, workspace_bytes, stream);
+}
+
+int muon_probe_mfma_bf16(int blocks, int iters, float* sink, hipStream_t stream) {
+  if (blocks < 1 || iters < 1 || !sink || !aligned(sink, 4)) return MUON_ERR_INVALID_ARG;
+  return launch_mfma_probe(blocks, iters, sink, stream) == hipSuccess ? MUON_OK : MUON_ERR_HIP;
+}
+
+int muon_probe_copy(const void* src, void* dst, size_t bytes, int blocks, hipStream_t stream) {
+  if (!src || !dst || blocks < 1 || bytes == 0 || bytes % 16 != 0 || !aligned(src, 16) ||
+      !aligned(dst, 16) || overlap(src, bytes, dst, bytes))
+    return MUON_ERR_INVALID_ARG;
+  return launch_copy_probe(src, dst, (long long)(bytes / 16), blocks, stream) == hipSuccess
+             ? MUON_OK
+             : MUON_ERR_HIP;
 }
 
 int muon_timing_enable(int on) { return g_timing.exchange(on ? 1 : 0); }

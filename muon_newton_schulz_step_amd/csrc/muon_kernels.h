@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include "muon.h"
+
 namespace muon {
 
 // Matrices handled by one launch when the launch needs per-matrix pointers.
@@ -170,5 +172,10 @@ hipError_t launch_normuon_rows(int compute_bf16, const NormuonArgs& a, const Row
                                int batch, hipStream_t s);
 hipError_t launch_apply(int compute_bf16, const ApplyArgs& a, const WeightTable& t,
                         int batch, hipStream_t s);
+
+// Measurement probes (muon_peaks.hip).
+hipError_t launch_mfma_probe(int blocks, int iters, float* sink, hipStream_t s);
+hipError_t launch_copy_probe(const void* src, void* dst, long long n16, int blocks,
+                             hipStream_t s);
 
 }  // namespace muon

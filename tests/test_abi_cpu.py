@@ -70,6 +70,10 @@ def orth(in_ptr=FAKE, in_dtype=0, out_ptr=FAKE * 2, out_dtype=1, batch=1, rows=8
     (dict(stride=8 * 16 - 1), mn.MUON_ERR_INVALID_ARG),
     (dict(in_ptr=FAKE + 2), mn.MUON_ERR_INVALID_ARG),   # misaligned
     (dict(out_ptr=FAKE + 8), mn.MUON_ERR_INVALID_ARG),  # overlaps input, not equal
+    # the same pointer but a wider output type: the output of matrix i
+    # would overwrite inputs of later matrices (or chunks) before they are read
+    (dict(out_ptr=FAKE, in_dtype=0, out_dtype=1), mn.MUON_ERR_INVALID_ARG),
+    (dict(out_ptr=FAKE, in_dtype=1, out_dtype=0, batch=100), mn.MUON_ERR_INVALID_ARG),
     (dict(rows=1 << 16, cols=1 << 16), mn.MUON_ERR_INVALID_ARG),  # too many elements
     (dict(ws=0), mn.MUON_ERR_WORKSPACE),
     (dict(ws_bytes=1024), mn.MUON_ERR_WORKSPACE),
@@ -246,3 +250,27 @@ def test_binding_refuses_host_tensors():
                    second_moments=[torch.zeros(8)], beta2=0.95, normuon_eps=1e-8)
     with pytest.raises(ValueError, match="GPU"):
         mn.orthogonalize(torch.zeros(8, 16))
+
+
+@pytest.mark.parametrize("blocks,iters,sink,expect", [
+    (0, 10, FAKE, mn.MUON_ERR_INVALID_ARG),
+    (4, 0, FAKE, mn.MUON_ERR_INVALID_ARG),
+    (4, 10, 0, mn.MUON_ERR_INVALID_ARG),
+    (4, 10, FAKE + 2, mn.MUON_ERR_INVALID_ARG),
+])
+def test_probe_mfma_rejects(blocks, iters, sink, expect):
+    assert mn.lib().muon_probe_mfma_bf16(blocks, iters, ctypes.c_void_p(sink), None) == expect
+
+
+@pytest.mark.parametrize("src,dst,nbytes,blocks", [
+    (0, FAKE * 4, 1024, 8),
+    (FAKE, 0, 1024, 8),
+    (FAKE, FAKE * 4, 1000, 8),        # not a multiple of 16
+    (FAKE + 8, FAKE * 4, 1024, 8),    # misaligned
+    (FAKE, FAKE + 512, 1024, 8),      # overlapping
+    (FAKE, FAKE * 4, 1024, 0),
+    (FAKE, FAKE * 4, 0, 8),
+])
+def test_probe_copy_rejects(src, dst, nbytes, blocks):
+    assert mn.lib().muon_probe_copy(ctypes.c_void_p(src), ctypes.c_void_p(dst), nbytes, blocks,
+                                    None) == mn.MUON_ERR_INVALID_ARG
