@@ -196,8 +196,9 @@ def ns_flops_executed(w, compute="bf16"):
 
 
 def is_step_kernel(name):
-    """A dispatch of the Muon step (the library's kernels minus its probes)."""
-    return "muon::" in name and "probe" not in name
+    """A dispatch of the Muon step (the library's kernels minus its probes);
+    rocprofv3 leaves some of the bf16 kernels' names mangled (_ZN4muon...)."""
+    return "muon" in name and "probe" not in name
 
 
 def per_dispatch_counters(path, counters):
@@ -228,8 +229,10 @@ def write_mfma(csv_path, w):
     probe_busy = probe[ctr[1]] / probe[ctr[2]]
     steps = [v for name, v in rows if is_step_kernel(name)]
     seq = launch_sequence(w)
-    if len(steps) != len(seq):
-        raise SystemExit(f"{len(steps)} library dispatches in {csv_path}, expected {len(seq)}")
+    if len(steps) == 0 or len(steps) % len(seq) != 0:
+        raise SystemExit(f"{len(steps)} library dispatches in {csv_path}, "
+                         f"not a multiple of the {len(seq)} of one step")
+    steps = steps[:len(seq)]  # the timed step (the instrumented pass repeats it)
     acc = {}
     for (kind, m, n), v in zip(seq, steps):
         a = acc.setdefault(f"{kind}_{m}x{n}", {"launches": 0, "flops": 0.0, "busy": 0.0,
@@ -279,8 +282,10 @@ def write_traffic(fetch_csv, write_csv, w):
         scale = COPY_BYTES / (copy_kib * 1024.0)
         out[field + "_scale"] = scale
         muon = [v for name, v in rows if is_step_kernel(name)]
-        if len(muon) != len(seq):
-            raise SystemExit(f"{len(muon)} library dispatches in {path}, expected {len(seq)}")
+        if len(muon) == 0 or len(muon) % len(seq) != 0:
+            raise SystemExit(f"{len(muon)} library dispatches in {path}, "
+                             f"not a multiple of the {len(seq)} of one step")
+        muon = muon[:len(seq)]  # the timed step (the instrumented pass repeats it)
         acc = {}
         for (kind, m, n), v in zip(seq, muon):
             a = acc.setdefault(f"{kind}_{m}x{n}", [0, 0.0])
@@ -391,18 +396,20 @@ def measure_peaks(torch, mn, dev):
     nbytes = 2 << 30
     src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
-    cblocks = 256 * 16
-    mn.probe_copy(src, dst, cblocks)  # warm-up
-    e0.record(stream)
-    moved = sum(mn.probe_copy(src, dst, cblocks) for _ in range(10))
-    e1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbs = moved / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    copy_gbs = 0.0
+    for cblocks in (256 * 4, 256 * 8, 256 * 16, 256 * 32):
+        mn.probe_copy(src, dst, cblocks)  # warm-up
+        e0.record(stream)
+        moved = sum(mn.probe_copy(src, dst, cblocks) for _ in range(10))
+        e1.record(stream)
+        torch.cuda.synchronize()
+        copy_gbs = max(copy_gbs, moved / (e0.elapsed_time(e1) * 1e-3) / 1e9)
     del src, dst, sink
     return {"mfma_bf16_tflops": round(mfma_tflops, 1), "copy_gbs": round(copy_gbs, 1),
             "how": "library probes on this GPU in this run: back-to-back "
                    "v_mfma_f32_32x32x16_bf16 on registers (1024 x 8 waves x 4 chains x "
-                   "1e5 rounds, 3 launches); 2 GiB copy in 16-byte accesses (10 launches)"}
+                   "1e5 rounds, 3 launches); 2 GiB copy in 16-byte accesses, 4 loads in "
+                   "flight per thread (10 launches each at 1024-8192 workgroups, the best)"}
 
 
 def main():

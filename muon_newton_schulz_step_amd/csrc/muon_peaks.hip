@@ -43,11 +43,21 @@ __global__ __launch_bounds__(512) void mfma_probe_kernel(int iters, float* sink)
   sink[(long long)blockIdx.x * blockDim.x + tid] = v;
 }
 
+// Grid-stride copy with four independent 16-byte loads in flight per thread
+// before their stores.
 __global__ __launch_bounds__(256) void copy_probe_kernel(const u32x4_t* __restrict__ src,
                                                          u32x4_t* __restrict__ dst, long long n16) {
   const long long stride = (long long)gridDim.x * blockDim.x;
-  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
-    dst[i] = src[i];
+  long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4_t v0 = src[i], v1 = src[i + stride], v2 = src[i + 2 * stride],
+                  v3 = src[i + 3 * stride];
+    dst[i] = v0;
+    dst[i + stride] = v1;
+    dst[i + 2 * stride] = v2;
+    dst[i + 3 * stride] = v3;
+  }
+  for (; i < n16; i += stride) dst[i] = src[i];
 }
 
 hipError_t launch_mfma_probe(int blocks, int iters, float* sink, hipStream_t s) {

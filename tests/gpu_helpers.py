@@ -68,3 +68,33 @@ def gram_closed_form(x0, coeffs, eig=None):
 def normalise(g, eps=1e-7):
     g = np.asarray(g, np.float64)
     return g / (math.sqrt(float(np.sum(g * g))) + eps)
+
+
+def tile_errors(y, ref, tile=256):
+    """Relative Frobenius error of every tile x tile block (ragged edge blocks
+    included; blocks whose reference is zero are skipped)."""
+    y = np.asarray(y, np.float64)
+    ref = np.asarray(ref, np.float64)
+    out = []
+    for i in range(0, ref.shape[0], tile):
+        for j in range(0, ref.shape[1], tile):
+            r = ref[i:i + tile, j:j + tile]
+            den = float(np.linalg.norm(r))
+            if den > 0.0:
+                out.append(float(np.linalg.norm(y[i:i + tile, j:j + tile] - r)) / den)
+    return np.array(out)
+
+
+# A fault confined to a few rows or one tile barely moves a large matrix's
+# whole-matrix error; each 256 x 256 tile is held to the bar as well, and to
+# 1.25x the matrix's own error (in the emulated bf16 path the tiles of one
+# matrix stay within 1.1x of it: tests/test_bf16_emulation.py).
+TILE_SPREAD = 1.25
+
+
+def check_tiles(y, ref, bound, what=""):
+    e = tile_errors(y, ref)
+    whole = float(np.linalg.norm(np.asarray(y, np.float64) - ref)) / float(np.linalg.norm(ref))
+    assert e.max() <= bound, (what, "tile", float(e.max()), int(e.argmax()))
+    assert e.max() <= TILE_SPREAD * whole + 1e-12, (what, "spread", float(e.max()), whole)
+    return float(e.max())

@@ -170,3 +170,26 @@ def test_qaq_gram_steps_one_and_three_only(kind):
     e13 = oracle.relative_frobenius_error(emulate(g, Q5, qaq_steps=(1, 3)), ref)
     e123 = oracle.relative_frobenius_error(emulate(g, Q5, qaq_steps=(1, 2, 3)), ref)
     assert e13 <= 0.5 * BF16_TOL and e123 > BF16_TOL, (e13, e123)
+
+
+@pytest.mark.parametrize("kind", ["gauss", "logspec"])
+@pytest.mark.parametrize("qaq", [(), (1, 3)])
+def test_tile_errors_track_the_matrix_error(kind, qaq):
+    """Every 256 x 256 tile of the emulated result is within 1.1x of the
+    whole matrix's error (the GPU tests allow 1.25x, gpu_helpers.check_tiles),
+    so a per-tile bound catches faults confined to part of a matrix."""
+    from gpu_helpers import TILE_SPREAD, tile_errors
+    g = (np.random.default_rng(3).standard_normal((512, 2048)).astype(np.float32)
+         if kind == "gauss" else _inputs(kind, 512, 2048, 13))
+    ref = oracle.orthogonalize(g.astype(np.float64), Q5)
+    o = emulate(g, Q5, qaq_steps=qaq)
+    whole = oracle.relative_frobenius_error(o, ref)
+    e = tile_errors(o, ref)
+    assert len(e) == 16 and e.max() <= 1.1 * whole and 1.1 < TILE_SPREAD
+    # a 10% error in one 32 x 256 block passes the whole-matrix bar but not
+    # the per-tile bound
+    bad = o.copy()
+    noise = np.sign(np.random.default_rng(4).standard_normal((32, 256)))
+    bad[64:96, :256] += 0.1 * ref[64:96, :256] * noise
+    assert oracle.relative_frobenius_error(bad, ref) <= BF16_TOL
+    assert tile_errors(bad, ref).max() > BF16_TOL

@@ -14,7 +14,7 @@ import torch
 import muon_newton_schulz_step_amd as mn
 import oracle
 import workloads as wl
-from gpu_helpers import BF16_TOL, announce
+from gpu_helpers import BF16_TOL, TILE_SPREAD, announce
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -57,8 +57,14 @@ def check(o, tall, cols, ref, scale=1.0):
     assert int(torch.count_nonzero(o)) == M  # nothing off the support
     assert np.all(got != 0.0)
     err = oracle.relative_frobenius_error(got, scale * ref)
-    print("  support rel err", err, flush=True)
+    # each block of 256 rows (256 support values) on its own too: a fault in
+    # a few rows barely moves the whole error (emulated blocks stay within
+    # 1.13x of it)
+    blocks = np.array([oracle.relative_frobenius_error(got[i:i + 256], scale * ref[i:i + 256])
+                       for i in range(0, M, 256)])
+    print("  support rel err", err, "worst 256-row block", blocks.max(), flush=True)
     assert err <= BF16_TOL
+    assert blocks.max() <= BF16_TOL and blocks.max() <= TILE_SPREAD * err
 
 
 @pytest.mark.parametrize("tall", [False, True], ids=["wide", "tall"])

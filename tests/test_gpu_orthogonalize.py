@@ -10,7 +10,7 @@ import torch
 import muon_newton_schulz_step_amd as mn
 import oracle
 import workloads as wl
-from gpu_helpers import announce, gram_closed_form, normalise, to64, tol
+from gpu_helpers import announce, check_tiles, gram_closed_form, normalise, to64, tol
 
 pytestmark = pytest.mark.gpu
 Q5 = [wl.QUINTIC] * 5
@@ -228,9 +228,11 @@ def test_gram_by_qaq_log_spectrum(tall):
     g = wl.make_grad(w, 0, device=DEV)
     o = mn.orthogonalize(g, Q5, compute="bf16", out_dtype=torch.float32)
     torch.cuda.synchronize()
-    err = oracle.relative_frobenius_error(to64(o), oracle.orthogonalize(to64(g), Q5))
+    ref = oracle.orthogonalize(to64(g), Q5)
+    err = oracle.relative_frobenius_error(to64(o), ref)
     print("  rel err", err, flush=True)
     assert err <= tol("bf16")
+    check_tiles(to64(o), ref, tol("bf16"), "qaq log spectrum")
 
 
 def test_gram_by_qaq_per_step_table():
@@ -241,6 +243,8 @@ def test_gram_by_qaq_per_step_table():
     g = wl.gaussian_matrix(2048, 8192, seed=41, device=DEV).to(torch.bfloat16)
     o = mn.orthogonalize(g, table, compute="bf16", out_dtype=torch.float32)
     torch.cuda.synchronize()
-    err = oracle.relative_frobenius_error(to64(o), oracle.orthogonalize(to64(g), table))
+    ref = oracle.orthogonalize(to64(g), table)
+    err = oracle.relative_frobenius_error(to64(o), ref)
     print("  rel err", err, flush=True)
     assert err <= tol("bf16")
+    check_tiles(to64(o), ref, tol("bf16"), "qaq per-step table")

@@ -34,7 +34,7 @@ def expected_dw(ref, w_before, dw_gpu, lr, scale, wd, cautious, o_gpu):
     o, w = ref["o"], w_before
     dw_keep = -lr * scale * o
     dw_decay = dw_keep - lr * wd * w
-    if not cautious:
+    if not cautious or wd == 0:
         return dw_decay
     mask = o * w >= 0
     dw = np.where(mask, dw_decay, dw_keep)
