@@ -17,7 +17,8 @@
  *  - Device pointers are caller-owned device memory; host pointers (shape
  *    arrays, pointer arrays, scales, coefficient tables) are read during the
  *    call only.  The library allocates no device memory: scratch comes from
- *    the caller's workspace, sized by the matching *_workspace_bytes query.
+ *    the caller's workspace, sized by the matching *_workspace_bytes query
+ *    (muon_step_static instead uses a fixed area the library holds).
  *  - Work is enqueued on `stream` (0 = the null stream) and is asynchronous:
  *    results are valid once the caller synchronises that stream.  The
  *    library never synchronises the device.
@@ -184,6 +185,27 @@ int muon_step_ex(int n, const int* rows, const int* cols,
                  const muon_coeff* coeffs, int n_steps, float eps, int compute,
                  const muon_options* options,
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ * muon_step with no workspace argument: its scratch is a fixed area of
+ * MUON_STATIC_SCRATCH_BYTES of device memory inside the library, one per GPU
+ * (the calling thread's current device; `stream` must belong to it), held
+ * from the first call on that GPU until the process ends.  The call itself
+ * allocates nothing.  Shapes whose muon_step_workspace_bytes exceeds
+ * MUON_STATIC_SCRATCH_BYTES return MUON_ERR_WORKSPACE before anything is
+ * enqueued.  Every call on one GPU uses that GPU's one area, which keeps the
+ * last call's contents (the step reads none of them): calls that overlap in
+ * time on one GPU (several streams, or host threads, at once) race and must
+ * be serialised by the caller.  Otherwise exactly muon_step: the same checks,
+ * the same kernels, bitwise the same results. */
+#define MUON_STATIC_SCRATCH_BYTES (256ull << 20)
+int muon_step_static(int n, const int* rows, const int* cols,
+                     void* const* params, int param_dtype,
+                     const void* const* grads, int grad_dtype,
+                     float* const* momentum, float mu, float lr, const float* scale,
+                     const muon_coeff* coeffs, int n_steps, float eps, int compute,
+                     hipStream_t stream);
 
 /* ------------------------------------------------------------ measurement */
 

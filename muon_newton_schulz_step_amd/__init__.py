@@ -8,6 +8,7 @@ which PyTorch-ROCm exposes as ``torch.cuda.current_stream().cuda_stream``).
     orthogonalize(x, coeffs)                       -> O for one matrix or a batch
     step(params, grads, bufs, mu=, lr=, scales=, coeffs=)   in place
     step_ex(..., weight_decay=, cautious=, second_moments=, beta2=, normuon_eps=)
+    step_static(params, grads, bufs, ...)          step with no workspace (fixed scratch)
 """
 from __future__ import annotations
 
@@ -16,7 +17,7 @@ import ctypes
 from . import _lib
 from ._lib import (  # noqa: F401
     EXPORTS, KERNEL_KINDS, MUON_BF16, MUON_FP32, MUON_MAX_STEPS, MUON_OK, MUON_ERR_HIP,
-    MUON_ERR_INVALID_ARG, MUON_ERR_UNSUPPORTED, MUON_ERR_WORKSPACE,
+    MUON_ERR_INVALID_ARG, MUON_ERR_UNSUPPORTED, MUON_ERR_WORKSPACE, MUON_STATIC_SCRATCH_BYTES,
 )
 
 DEFAULT_EPS = 1e-7
@@ -276,6 +277,45 @@ def _step(params, grads, bufs, second_moments, opt, *, mu, lr, scales, coeffs, n
             where = "muon_step_ex"
     if st != MUON_OK:
         raise MuonError(st, where)
+
+
+def step_static(params, grads, bufs, *, mu, lr, scales=None, coeffs=QUINTIC, n_steps=None,
+                eps=DEFAULT_EPS, compute="bf16"):
+    """``step`` through muon_step_static: no workspace, nothing allocated; the
+    scratch is the library's fixed area on the current GPU
+    (MUON_STATIC_SCRATCH_BYTES), so calls that overlap in time on one GPU
+    race."""
+    n = len(params)
+    if not (len(grads) == len(bufs) == n):
+        raise ValueError("params, grads and bufs must have the same length")
+    if n == 0:
+        return
+    if n_steps is None and isinstance(coeffs[0], (int, float)):
+        n_steps = 5
+    table, n_steps = _coeffs(coeffs, n_steps)
+    if scales is None:
+        scales = [1.0] * n
+    grad_dtype = _dtype_code(grads[0].dtype)
+    for p, g, b in zip(params, grads, bufs):
+        if p.dim() != 2 or g.shape != p.shape or b.shape != p.shape:
+            raise ValueError("params, grads and bufs must be matching 2-D tensors")
+        if not (p.is_contiguous() and g.is_contiguous() and b.is_contiguous()):
+            raise ValueError("tensors must be contiguous")
+        if _dtype_code(g.dtype) != grad_dtype:
+            raise ValueError("all grads must share one dtype")
+    device = params[0].device
+    _check_device(device, params=params, grads=grads, bufs=bufs)
+    rows = _lib.int_array(p.shape[0] for p in params)
+    cols = _lib.int_array(p.shape[1] for p in params)
+    with _torch().cuda.device(device):
+        st = lib().muon_step_static(
+            n, rows, cols, _lib.ptr_array(p.data_ptr() for p in params),
+            _dtype_code(params[0].dtype), _lib.ptr_array(g.data_ptr() for g in grads), grad_dtype,
+            _lib.ptr_array(b.data_ptr() for b in bufs), float(mu), float(lr),
+            _lib.float_array(scales), table, n_steps, float(eps), _compute_code(compute),
+            _stream(device))
+    if st != MUON_OK:
+        raise MuonError(st, "muon_step_static")
 
 
 def probe_mfma_bf16(sink, blocks: int, iters: int) -> float:

@@ -12,6 +12,7 @@ MUON_OK, MUON_ERR_INVALID_ARG, MUON_ERR_UNSUPPORTED, MUON_ERR_WORKSPACE, MUON_ER
 MUON_MAX_STEPS = 64
 MUON_WORKSPACE_ALIGN = 256
 MUON_PTR_ALIGN = 16
+MUON_STATIC_SCRATCH_BYTES = 256 << 20
 KERNEL_KINDS = ("prep", "norm", "gram", "poly", "update", "final", "normuon", "apply",
                 "gramq")
 
@@ -25,6 +26,7 @@ EXPORTS = (
     "muon_step",
     "muon_step_ex_workspace_bytes",
     "muon_step_ex",
+    "muon_step_static",
     "muon_timing_enable",
     "muon_timing_read",
     "muon_probe_mfma_bf16",
@@ -95,6 +97,12 @@ def load() -> ctypes.CDLL:
         ctypes.POINTER(MuonCoeff), ctypes.c_int, ctypes.c_float, ctypes.c_int,
         ctypes.POINTER(MuonOptions), _vp, ctypes.c_size_t, _vp]
     lib.muon_step_ex.restype = ctypes.c_int
+    lib.muon_step_static.argtypes = [
+        ctypes.c_int, _c_int_p, _c_int_p, ctypes.POINTER(_vp), ctypes.c_int,
+        ctypes.POINTER(_vp), ctypes.c_int, ctypes.POINTER(_vp), ctypes.c_float,
+        ctypes.c_float, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(MuonCoeff),
+        ctypes.c_int, ctypes.c_float, ctypes.c_int, _vp]
+    lib.muon_step_static.restype = ctypes.c_int
     lib.muon_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, _vp, _vp]
     lib.muon_probe_mfma_bf16.restype = ctypes.c_int
     lib.muon_probe_copy.argtypes = [_vp, _vp, ctypes.c_size_t, ctypes.c_int, _vp]

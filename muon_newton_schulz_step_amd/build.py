@@ -22,6 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmuon.so")
 SOURCES = ["gemm_update.hip", "gemm_final_w.hip", "gemm_final_out.hip", "gemm_gram.hip",
            "gemm_poly.hip", "gemm_fp32.hip", "muon_kernels.hip", "muon_peaks.hip",
+           "muon_static.hip",
            "muon_api.cpp"]
 ARCH = os.environ.get("MUON_OFFLOAD_ARCH", "gfx950")
 

@@ -473,13 +473,15 @@ int check_options(const muon_options* o) {
   return MUON_OK;
 }
 
-// muon_step and muon_step_ex (opt == nullptr: the plain step).
+// muon_step and muon_step_ex (opt == nullptr: the plain step).  With a
+// workspace source `src` (muon_step_static), the workspace arguments are
+// ignored and the source is asked for one once every argument has passed.
 int step_impl(int n, const int* rows, const int* cols, void* const* params, int param_dtype,
               const void* const* grads, int grad_dtype, float* const* momentum,
               float* const* second_moment, float mu, float lr, const float* scale,
               const muon_coeff* coeffs, int n_steps, float eps, int compute,
               const muon_options* opt, void* workspace, size_t workspace_bytes,
-              hipStream_t stream) {
+              hipStream_t stream, const WorkspaceSource* src = nullptr) {
   if (n < 0) return MUON_ERR_INVALID_ARG;
   if (!is_dtype(param_dtype) || !is_dtype(grad_dtype) || !is_dtype(compute))
     return MUON_ERR_INVALID_ARG;
@@ -515,6 +517,9 @@ int step_impl(int n, const int* rows, const int* cols, void* const* params, int 
   if (param_dtype != MUON_FP32) return MUON_ERR_UNSUPPORTED;
   const size_t need = step_ws_bytes(n, rows, cols, compute, normuon);
   if (need == 0) return MUON_ERR_INVALID_ARG;
+  if (src) {
+    if (int st = src->get(need, &workspace, &workspace_bytes)) return st;
+  }
   if (!workspace || workspace_bytes < need || !aligned(workspace, kWsAlign))
     return MUON_ERR_WORKSPACE;
   for (int i = 0; i < n; ++i) {
@@ -578,6 +583,17 @@ int step_impl(int n, const int* rows, const int* cols, void* const* params, int 
 }
 
 }  // namespace
+
+namespace muon {
+int step_with_source(int n, const int* rows, const int* cols, void* const* params,
+                     int param_dtype, const void* const* grads, int grad_dtype,
+                     float* const* momentum, float mu, float lr, const float* scale,
+                     const muon_coeff* coeffs, int n_steps, float eps, int compute,
+                     const WorkspaceSource& src, hipStream_t stream) {
+  return step_impl(n, rows, cols, params, param_dtype, grads, grad_dtype, momentum, nullptr, mu,
+                   lr, scale, coeffs, n_steps, eps, compute, nullptr, nullptr, 0, stream, &src);
+}
+}  // namespace muon
 
 extern "C" {
 

@@ -178,4 +178,20 @@ hipError_t launch_mfma_probe(int blocks, int iters, float* sink, hipStream_t s);
 hipError_t launch_copy_probe(const void* src, void* dst, long long n16, int blocks,
                              hipStream_t s);
 
+// Where a step's workspace comes from when the caller passes none
+// (muon_step_static): asked once every argument has passed its checks, for
+// `need` bytes; returns a muon_status.
+struct WorkspaceSource {
+  int (*get_fn)(const void* ctx, size_t need, void** ws, size_t* bytes);
+  const void* ctx;
+  int get(size_t need, void** ws, size_t* bytes) const { return get_fn(ctx, need, ws, bytes); }
+};
+
+// muon_step with its workspace from `src` (muon_api.cpp).
+int step_with_source(int n, const int* rows, const int* cols, void* const* params,
+                     int param_dtype, const void* const* grads, int grad_dtype,
+                     float* const* momentum, float mu, float lr, const float* scale,
+                     const muon_coeff* coeffs, int n_steps, float eps, int compute,
+                     const WorkspaceSource& src, hipStream_t stream);
+
 }  // namespace muon

@@ -252,6 +252,53 @@ def test_binding_refuses_host_tensors():
         mn.orthogonalize(torch.zeros(8, 16))
 
 
+def static_call(n=2, rows=(8, 16), cols=(16, 8), params=None, grads=None, bufs=None,
+                param_dtype=1, grad_dtype=0, mu=0.95, lr=0.02, scales=None, coeffs=Q,
+                n_steps=None, eps=1e-7, compute=0):
+    lib = mn.lib()
+    params = params if params is not None else [FAKE * (i + 1) * 64 for i in range(n)]
+    grads = grads if grads is not None else [FAKE * (i + 1) * 64 + 4096 for i in range(n)]
+    bufs = bufs if bufs is not None else [FAKE * (i + 1) * 64 + 8192 for i in range(n)]
+    scales = scales if scales is not None else [1.0] * n
+    if n_steps is None:
+        n_steps = len(coeffs)
+    return lib.muon_step_static(
+        n, _lib.int_array(rows), _lib.int_array(cols), _lib.ptr_array(params), param_dtype,
+        _lib.ptr_array(grads), grad_dtype, _lib.ptr_array(bufs), mu, lr,
+        _lib.float_array(scales), _lib.coeff_array(coeffs), n_steps, eps, compute, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(n=-1), mn.MUON_ERR_INVALID_ARG),
+    (dict(n=0), mn.MUON_OK),
+    (dict(rows=(8, 0)), mn.MUON_ERR_INVALID_ARG),
+    (dict(params=[FAKE * 64, 0]), mn.MUON_ERR_INVALID_ARG),
+    (dict(bufs=[FAKE * 64, FAKE * 128 + 8192]), mn.MUON_ERR_INVALID_ARG),
+    (dict(param_dtype=0), mn.MUON_ERR_UNSUPPORTED),
+    (dict(mu=float("nan")), mn.MUON_ERR_INVALID_ARG),
+    (dict(n_steps=65, coeffs=Q * 13), mn.MUON_ERR_INVALID_ARG),
+    # one 3072 x 12288 matrix needs more than the fixed scratch area: refused
+    # before anything touches the GPU
+    (dict(n=1, rows=(3072,), cols=(12288,), params=[1 << 40], grads=[2 << 40],
+          bufs=[3 << 40]), mn.MUON_ERR_WORKSPACE),
+])
+def test_step_static_rejects_before_enqueue(kw, expect):
+    assert static_call(**kw) == expect
+
+
+def test_static_scratch_size_matches_header():
+    src = open(os.path.join(ROOT, "include", "muon.h")).read()
+    m = re.search(r"#define MUON_STATIC_SCRATCH_BYTES \((\d+)ull << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.MUON_STATIC_SCRATCH_BYTES
+    lib = mn.lib()
+    # the limit is the workspace of muon_step: the 8-layer d768 GPT set fits,
+    # one (3072, 12288) matrix does not
+    d768 = [(768, 768), (768, 768), (768, 768), (768, 768), (3072, 768), (768, 3072)] * 8
+    assert 0 < mn.step_workspace_bytes(d768) <= _lib.MUON_STATIC_SCRATCH_BYTES
+    big = lib.muon_step_workspace_bytes(1, _lib.int_array([3072]), _lib.int_array([12288]), 0)
+    assert big > _lib.MUON_STATIC_SCRATCH_BYTES
+
+
 @pytest.mark.parametrize("blocks,iters,sink,expect", [
     (0, 10, FAKE, mn.MUON_ERR_INVALID_ARG),
     (4, 0, FAKE, mn.MUON_ERR_INVALID_ARG),
