@@ -97,14 +97,24 @@ __device__ __forceinline__ void wait_vmcnt() {
 #endif
 }
 
+// Wait until this wave has no vector-memory operation and no LDS operation in
+// flight: s_waitcnt vmcnt(0) lgkmcnt(0) (expcnt untouched).
+__device__ __forceinline__ void wait_vm_lgkm0() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_s_waitcnt((7 << 4));
+#endif
+}
+
 // Workgroup barrier for the direct-to-LDS pipeline, without memory fences:
 // a fence would wait for every outstanding load, including the loads of
-// later k-tiles that must stay in flight.  It is sufficient here because
-// (1) each wave waits (vmcnt) for its own loads of the k-tile about to be
-// read before arriving, and LDS has no cache, so the data is in place for
-// every wave once all have arrived; (2) a wave's LDS reads of the stage that
-// is reloaded next have returned before its MFMAs consumed them.  The
-// "memory" clobber keeps the compiler from moving LDS accesses across it.
+// later k-tiles that must stay in flight.  It is sufficient here because,
+// before arriving, each wave waits (wait_vm_lgkm0) for (1) its own loads of
+// the k-tile about to be read (LDS has no cache, so the data is in place for
+// every wave once all have arrived) and (2) its own LDS reads of the stage
+// that the waves refill right after the barrier: an LDS read still queued
+// when another wave's direct-to-LDS load lands would return the next
+// k-tile's data.  The "memory" clobber keeps the compiler from moving LDS
+// accesses across it.
 __device__ __forceinline__ void barrier_no_fence() {
 #if defined(__HIP_DEVICE_COMPILE__)
   asm volatile("s_barrier" ::: "memory");
@@ -430,8 +440,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
         mfmas(kk & 1);
       }
       schedule_substeps(KK - 1);
-      wait_vmcnt<0>();     // this wave's part of k-tile kt+1 has landed
-      barrier_no_fence();  // everyone's has; everyone is done reading cur
+      wait_vm_lgkm0();     // this wave's part of k-tile kt+1 has landed and
+                           // its reads of cur have returned
+      barrier_no_fence();  // everyone's has: cur may be refilled
       issue(kt + 2 < nk ? kt + 2 : nk - 1, cur);
       fload(nxt, 0, 0);
       mfmas((KK - 1) & 1);
