@@ -30,6 +30,11 @@
  *  - Repeated calls on the same inputs give bitwise-identical results (all
  *    reductions use a fixed order; there are no floating-point atomics).
  *  - Calls are re-entrant when they use distinct workspaces.
+ *  - A step whose chunks are all small runs them concurrently: on the
+ *    caller's stream and up to three library-owned streams per device
+ *    (default priority), forked off the caller's stream with an event and
+ *    joined back to it before the call returns, so stream order and graph
+ *    capture see one step as usual.
  */
 #ifndef MUON_H
 #define MUON_H
@@ -71,8 +76,11 @@ const char* muon_status_string(int status);
  * rows x cols with the given compute precision.  0 for invalid sizes. */
 size_t muon_orthogonalize_workspace_bytes(int batch, int rows, int cols, int compute);
 
-/* Bytes of workspace muon_step needs for the n matrices rows[i] x cols[i].
- * 0 for invalid sizes or n == 0. */
+/* Bytes of workspace muon_step needs for the n matrices rows[i] x cols[i]:
+ * the largest of its chunks (matrices of one oriented shape, at most 64 per
+ * chunk) when the chunks run one after the other, their sum when a small
+ * step runs them concurrently (every chunk small enough to leave most of the
+ * chip idle on its own).  0 for invalid sizes or n == 0. */
 size_t muon_step_workspace_bytes(int n, const int* rows, const int* cols, int compute);
 
 /* The grouping muon_step uses (page 1: momentum stacked per shape group).

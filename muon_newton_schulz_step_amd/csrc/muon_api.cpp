@@ -445,20 +445,110 @@ bool overlap(const void* p, size_t pb, const void* q, size_t qb) {
   return a < b + qb && b < a + pb;
 }
 
-size_t step_ws_bytes(int n, const int* rows, const int* cols, int compute, bool normuon) {
+// A step's chunks in launch order: each oriented-shape group split into
+// chunks of at most kChunk matrices.
+struct ChunkRef {
+  int g, b0, cnt;
+};
+
+void list_chunks(const std::vector<Group>& groups, std::vector<ChunkRef>& out) {
+  out.clear();
+  for (int g = 0; g < (int)groups.size(); ++g) {
+    const int total = (int)groups[g].idx.size();
+    for (int b0 = 0; b0 < total; b0 += kChunk)
+      out.push_back(ChunkRef{g, b0, total - b0 < kChunk ? total - b0 : kChunk});
+  }
+}
+
+// MUON_CONCURRENT=0|1 forces the chunks of a step to run one after the
+// other or concurrently (a tuning knob; see concurrent_chunks).
+int concurrent_pref() {
+  static const int v = [] {
+    const char* e = std::getenv("MUON_CONCURRENT");
+    return e ? (std::atoi(e) != 0 ? 1 : 0) : -1;
+  }();
+  return v;
+}
+
+// A chunk whose update does fewer multiply-adds than this (count x M x N x M,
+// padded) leaves most of the chip idle in every launch: 32 matrices of
+// 768 x 768 run 21 or 36 tiles of 128 x 128 per matrix.  A step made only of
+// such chunks runs them concurrently, each on its own stream lane and in its
+// own workspace region; larger chunks fill the chip by themselves and run one
+// after the other (concurrent large groups evict each other's operand panels
+// from L2).
+constexpr double kConcurrentMacs = 1e11;
+
+bool concurrent_chunks(const std::vector<Group>& groups, const std::vector<ChunkRef>& chunks) {
+  if (chunks.size() < 2) return false;
+  if (concurrent_pref() >= 0) return concurrent_pref() == 1;
+  for (const ChunkRef& c : chunks) {
+    const double M = (double)pad_dim(groups[c.g].m), N = (double)pad_dim(groups[c.g].n);
+    if (c.cnt * M * N * M >= kConcurrentMacs) return false;
+  }
+  return true;
+}
+
+// Workspace of a step: the largest chunk's layout when chunks run one after
+// the other, the sum of them (each chunk in its own region, in chunk order)
+// when they run concurrently.  `offsets` (if given) receives each chunk's
+// region.  0 for invalid sizes.
+size_t step_ws_bytes(int n, const int* rows, const int* cols, int compute, bool normuon,
+                     bool allow_concurrent = true, std::vector<size_t>* offsets = nullptr,
+                     bool* concurrent = nullptr) {
   if (n < 1 || !rows || !cols || !is_dtype(compute)) return 0;
   for (int i = 0; i < n; ++i)
     if (!shape_ok(rows[i], cols[i])) return 0;
   std::vector<Group> groups;
   plan(n, rows, cols, groups, nullptr);
-  size_t best = 0;
-  for (const Group& g : groups) {
-    const int cnt = (int)g.idx.size() < kChunk ? (int)g.idx.size() : kChunk;
+  std::vector<ChunkRef> chunks;
+  list_chunks(groups, chunks);
+  const bool conc = allow_concurrent && concurrent_chunks(groups, chunks);
+  if (concurrent) *concurrent = conc;
+  if (offsets) offsets->clear();
+  size_t best = 0, sum = 0;
+  for (const ChunkRef& c : chunks) {
     Layout L;
-    if (!make_layout(cnt, g.m, g.n, compute == MUON_BF16, L, normuon)) return 0;
+    if (!make_layout(c.cnt, groups[c.g].m, groups[c.g].n, compute == MUON_BF16, L, normuon))
+      return 0;
+    if (offsets) offsets->push_back(conc ? sum : 0);
+    sum += align_up(L.total, kWsAlign);
     if (L.total > best) best = L.total;
   }
-  return best;
+  return conc ? sum : best;
+}
+
+// Stream lanes for concurrent chunks: per device, kLanes - 1 library streams
+// (default priority, non-blocking) beside the caller's, with the events that
+// fork them off the caller's stream and join them back (a pattern HIP graph
+// capture records as parallel branches).  The per-device mutex keeps one
+// call's fork, launches and join together when several host threads step at
+// once.
+constexpr int kLanes = 4;
+constexpr int kMaxDevices = 64;
+struct Lanes {
+  std::mutex mu;
+  bool ready = false;
+  hipStream_t s[kLanes - 1];
+  hipEvent_t fork, join[kLanes - 1];
+};
+Lanes g_lanes[kMaxDevices];
+std::mutex g_lanes_init;
+
+Lanes* lanes_of_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_lanes_init);
+  Lanes& L = g_lanes[dev];
+  if (!L.ready) {
+    for (int i = 0; i < kLanes - 1; ++i)
+      if (hipStreamCreateWithFlags(&L.s[i], hipStreamNonBlocking) != hipSuccess ||
+          hipEventCreateWithFlags(&L.join[i], hipEventDisableTiming) != hipSuccess)
+        return nullptr;
+    if (hipEventCreateWithFlags(&L.fork, hipEventDisableTiming) != hipSuccess) return nullptr;
+    L.ready = true;
+  }
+  return &L;
 }
 
 int check_options(const muon_options* o) {
@@ -515,7 +605,11 @@ int step_impl(int n, const int* rows, const int* cols, void* const* params, int 
     }
   }
   if (param_dtype != MUON_FP32) return MUON_ERR_UNSUPPORTED;
-  const size_t need = step_ws_bytes(n, rows, cols, compute, normuon);
+  // the allocation-free entry point never forks: its scratch holds one chunk
+  std::vector<size_t> ws_off;
+  bool conc = false;
+  const size_t need = step_ws_bytes(n, rows, cols, compute, normuon, src == nullptr, &ws_off,
+                                    &conc);
   if (need == 0) return MUON_ERR_INVALID_ARG;
   if (src) {
     if (int st = src->get(need, &workspace, &workspace_bytes)) return st;
@@ -535,51 +629,76 @@ int step_impl(int n, const int* rows, const int* cols, void* const* params, int 
   const bool cbf16 = compute == MUON_BF16;
   std::vector<Group> groups;
   plan(n, rows, cols, groups, nullptr);
+  std::vector<ChunkRef> chunks;
+  list_chunks(groups, chunks);
   char* ws = static_cast<char*>(workspace);
-  for (const Group& g : groups) {
-    const int total = (int)g.idx.size();
-    for (int b0 = 0; b0 < total; b0 += kChunk) {
-      const int cnt = total - b0 < kChunk ? total - b0 : kChunk;
-      // Tall and wide matrices of one oriented shape share the launch: the
-      // kernels read each matrix's orientation from the mask.
-      Chunk c{};
-      // wide matrices first, then the tall ones (the last step launches the
-      // two orientations separately, each over a contiguous range)
-      int order[kChunk];
-      int no = 0;
-      for (int pass = 0; pass < 2; ++pass)
-        for (int q = 0; q < cnt; ++q) {
-          const int i = g.idx[b0 + q];
-          if ((rows[i] > cols[i]) == (pass == 1)) order[no++] = i;
-        }
-      for (int q = 0; q < cnt; ++q) {
-        const int i = order[q];
-        c.pt.g[q] = grads[i];
-        c.pt.buf[q] = momentum[i];
-        c.wt.w[q] = static_cast<float*>(params[i]);
-        c.wt.scale[q] = scale[i];
-        if (normuon) c.vt.v[q] = second_moment[i];
-        if (rows[i] > cols[i]) c.tall_mask |= 1ull << q;
-      }
-      Layout L;
-      make_layout(cnt, g.m, g.n, cbf16, L, normuon);
-      c.cnt = cnt;
-      c.momentum = true;
-      c.in_bf16 = grad_dtype == MUON_BF16;
-      c.mu = mu;
-      c.final_mode = FINAL_WEIGHTS;
-      c.neg_lr = -lr;
-      if (opt) {
-        c.neg_lrwd = -lr * opt->weight_decay;
-        c.cautious = opt->cautious;
-        c.normuon = opt->normuon;
-        c.beta2 = opt->beta2;
-        c.eps2 = opt->normuon_eps;
-      }
-      if (int st = run_chunk(c, L, ws, coeffs, n_steps, eps, cbf16, stream)) return st;
+
+  // Concurrent chunks: lane 0 is the caller's stream, the others fork off it
+  // and are joined back to it at the end (also after a failed launch, so
+  // that a stream capture is never left with unjoined branches).
+  hipStream_t lane[kLanes] = {stream};
+  int nlanes = 1;
+  Lanes* lanes = nullptr;
+  std::unique_lock<std::mutex> lane_lock;
+  if (conc) {
+    lanes = lanes_of_current_device();
+    if (!lanes) return MUON_ERR_HIP;
+    lane_lock = std::unique_lock<std::mutex>(lanes->mu);
+    nlanes = (int)chunks.size() < kLanes ? (int)chunks.size() : kLanes;
+    if (hipEventRecord(lanes->fork, stream) != hipSuccess) return MUON_ERR_HIP;
+    for (int l = 1; l < nlanes; ++l) {
+      lane[l] = lanes->s[l - 1];
+      if (hipStreamWaitEvent(lane[l], lanes->fork, 0) != hipSuccess) return MUON_ERR_HIP;
     }
   }
-  return MUON_OK;
+  int status = MUON_OK;
+  for (size_t ci = 0; ci < chunks.size() && status == MUON_OK; ++ci) {
+    const Group& g = groups[chunks[ci].g];
+    const int b0 = chunks[ci].b0, cnt = chunks[ci].cnt;
+    // Tall and wide matrices of one oriented shape share the launch: the
+    // kernels read each matrix's orientation from the mask.
+    Chunk c{};
+    // wide matrices first, then the tall ones (the last step launches the
+    // two orientations separately, each over a contiguous range)
+    int order[kChunk];
+    int no = 0;
+    for (int pass = 0; pass < 2; ++pass)
+      for (int q = 0; q < cnt; ++q) {
+        const int i = g.idx[b0 + q];
+        if ((rows[i] > cols[i]) == (pass == 1)) order[no++] = i;
+      }
+    for (int q = 0; q < cnt; ++q) {
+      const int i = order[q];
+      c.pt.g[q] = grads[i];
+      c.pt.buf[q] = momentum[i];
+      c.wt.w[q] = static_cast<float*>(params[i]);
+      c.wt.scale[q] = scale[i];
+      if (normuon) c.vt.v[q] = second_moment[i];
+      if (rows[i] > cols[i]) c.tall_mask |= 1ull << q;
+    }
+    Layout L;
+    make_layout(cnt, g.m, g.n, cbf16, L, normuon);
+    c.cnt = cnt;
+    c.momentum = true;
+    c.in_bf16 = grad_dtype == MUON_BF16;
+    c.mu = mu;
+    c.final_mode = FINAL_WEIGHTS;
+    c.neg_lr = -lr;
+    if (opt) {
+      c.neg_lrwd = -lr * opt->weight_decay;
+      c.cautious = opt->cautious;
+      c.normuon = opt->normuon;
+      c.beta2 = opt->beta2;
+      c.eps2 = opt->normuon_eps;
+    }
+    status = run_chunk(c, L, ws + ws_off[ci], coeffs, n_steps, eps, cbf16, lane[ci % nlanes]);
+  }
+  for (int l = 1; l < nlanes; ++l) {
+    if (hipEventRecord(lanes->join[l - 1], lane[l]) != hipSuccess ||
+        hipStreamWaitEvent(stream, lanes->join[l - 1], 0) != hipSuccess)
+      status = MUON_ERR_HIP;
+  }
+  return status;
 }
 
 }  // namespace

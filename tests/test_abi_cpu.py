@@ -291,10 +291,12 @@ def test_static_scratch_size_matches_header():
     m = re.search(r"#define MUON_STATIC_SCRATCH_BYTES \((\d+)ull << (\d+)\)", src)
     assert m and int(m.group(1)) << int(m.group(2)) == _lib.MUON_STATIC_SCRATCH_BYTES
     lib = mn.lib()
-    # the limit is the workspace of muon_step: the 8-layer d768 GPT set fits,
-    # one (3072, 12288) matrix does not
-    d768 = [(768, 768), (768, 768), (768, 768), (768, 768), (3072, 768), (768, 3072)] * 8
-    assert 0 < mn.step_workspace_bytes(d768) <= _lib.MUON_STATIC_SCRATCH_BYTES
+    # the limit applies to the largest chunk (the static entry point runs its
+    # chunks one after the other): the 8-layer d768 GPT set fits, one
+    # (3072, 12288) matrix does not
+    largest = max(mn.orthogonalize_workspace_bytes(32, 768, 768),
+                  mn.orthogonalize_workspace_bytes(16, 768, 3072))
+    assert 0 < largest <= _lib.MUON_STATIC_SCRATCH_BYTES
     big = lib.muon_step_workspace_bytes(1, _lib.int_array([3072]), _lib.int_array([12288]), 0)
     assert big > _lib.MUON_STATIC_SCRATCH_BYTES
 
@@ -321,3 +323,20 @@ def test_probe_mfma_rejects(blocks, iters, sink, expect):
 def test_probe_copy_rejects(src, dst, nbytes, blocks):
     assert mn.lib().muon_probe_copy(ctypes.c_void_p(src), ctypes.c_void_p(dst), nbytes, blocks,
                                     None) == mn.MUON_ERR_INVALID_ARG
+
+
+def test_small_steps_size_a_region_per_chunk():
+    """Small steps run their chunks concurrently, each in its own workspace
+    region: the size is the sum of the chunks' layouts; large steps run them
+    in turn and need only the largest."""
+    d768 = [(768, 768)] * 4 + [(3072, 768), (768, 3072)]
+    d768 = d768 * 8
+    a = mn.orthogonalize_workspace_bytes(32, 768, 768)
+    b = mn.orthogonalize_workspace_bytes(16, 768, 3072)
+    assert mn.step_workspace_bytes(d768) == a + b
+    big = [(3072, 3072), (3072, 12288)] * 2
+    assert mn.step_workspace_bytes(big) == max(
+        mn.orthogonalize_workspace_bytes(2, 3072, 3072),
+        mn.orthogonalize_workspace_bytes(2, 3072, 12288))
+    # one chunk: nothing to run beside it
+    assert mn.step_workspace_bytes([(768, 768)] * 3) == mn.orthogonalize_workspace_bytes(3, 768, 768)

@@ -37,6 +37,18 @@ def both_ways(w, compute):
     assert not torch.equal(b["params"][0], w0)
 
 
+def static_need(shapes, compute):
+    """Scratch of muon_step_static: its chunks run one after the other, so
+    the largest chunk's workspace (one chunk = up to 64 matrices of one
+    oriented shape)."""
+    groups = {}
+    for r, c in shapes:
+        key = (min(r, c), max(r, c))
+        groups[key] = groups.get(key, 0) + 1
+    return max(mn.orthogonalize_workspace_bytes(min(cnt, 64), m, n, compute)
+               for (m, n), cnt in groups.items())
+
+
 def largest_d768_prefix(compute):
     """The most whole layers of the d768 GPT set whose step fits the fixed
     scratch area (all 8 on the bf16 path; fp32 carries X in 12 bytes per
@@ -44,7 +56,7 @@ def largest_d768_prefix(compute):
     per_layer = 6
     for layers in range(8, 0, -1):
         shapes = wl.GPT_D768.shapes[:layers * per_layer]
-        if mn.step_workspace_bytes(shapes, compute) <= mn.MUON_STATIC_SCRATCH_BYTES:
+        if static_need(shapes, compute) <= mn.MUON_STATIC_SCRATCH_BYTES:
             return dataclasses.replace(wl.GPT_D768, shapes=shapes)
     raise AssertionError("not even one d768 layer fits")
 
