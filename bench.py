@@ -53,6 +53,13 @@ def parse():
     p.add_argument("--workload", default="gpt_3.8b_28layers")
     p.add_argument("--compute", default="bf16", choices=["bf16", "fp32"])
     p.add_argument("--variant", default="plain", choices=list(VARIANTS))
+    p.add_argument("--coeffs", choices=["quintic", "cubic"], default=None,
+                   help="coefficient triple at every step (default: the workload's quintic)")
+    p.add_argument("--ns-steps", type=int, default=None,
+                   help="Newton-Schulz steps (default: the workload's 5)")
+    p.add_argument("--matrices", type=int, default=None,
+                   help="time a bounded sample: the first N matrices of each raw shape of "
+                        "the workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--graph", action="store_true",
                    help="time replays of one captured step (a HIP graph: no per-launch host "
@@ -424,6 +431,15 @@ def main():
     import workloads as wl
 
     w = wl.WORKLOADS[args.workload]
+    full_count = len(w.shapes)
+    if args.coeffs or args.ns_steps or args.matrices:
+        import dataclasses
+        w = dataclasses.replace(
+            w, coeffs={"quintic": wl.QUINTIC, "cubic": wl.CUBIC}[args.coeffs or "quintic"]
+            if args.coeffs else w.coeffs,
+            n_steps=args.ns_steps or w.n_steps,
+            shapes=(tuple(w.shapes[i] for i in wl.sample_indices(w, args.matrices))
+                    if args.matrices else w.shapes))
     if args.write_traffic:
         write_traffic(args.write_traffic[0], args.write_traffic[1], w)
         return
@@ -547,7 +563,9 @@ def main():
         "vs_baseline": None,
         "dtype": args.compute,
         "data": "synthetic (seeded, generated on the GPU)",
-        "config": {"workload": w.name, "matrices": len(w.shapes), "variant": args.variant,
+        "config": {"workload": w.name, "matrices": len(w.shapes),
+                   **({"sample_of": full_count} if len(w.shapes) != full_count else {}),
+                   "variant": args.variant,
                    **({"options": opt} if opt else {}),
                    "oriented_groups": {f"{m}x{n}": c for (m, n), c in groups.items()},
                    "ns_steps": w.n_steps, "coeffs": list(w.coeffs),

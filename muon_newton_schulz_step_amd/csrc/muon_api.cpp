@@ -471,13 +471,13 @@ int concurrent_pref() {
 }
 
 // A chunk whose update does fewer multiply-adds than this (count x M x N x M,
-// padded) leaves most of the chip idle in every launch: 32 matrices of
-// 768 x 768 run 21 or 36 tiles of 128 x 128 per matrix.  A step made only of
-// such chunks runs them concurrently, each on its own stream lane and in its
-// own workspace region; larger chunks fill the chip by themselves and run one
-// after the other (concurrent large groups evict each other's operand panels
-// from L2).
-constexpr double kConcurrentMacs = 1e11;
+// padded) is short, and its launches end in partly idle rounds of tiles.  A
+// step made only of such chunks runs them concurrently, each on its own
+// stream lane and in its own workspace region, so one chunk's tail overlaps
+// another's work (d768 GPT set 1.73 -> 1.67 ms, d1280 12.69 -> 12.41 ms);
+// larger chunks run one after the other (concurrent large groups evict each
+// other's operand panels from L2: the 3.8B set got slower).
+constexpr double kConcurrentMacs = 5e11;
 
 bool concurrent_chunks(const std::vector<Group>& groups, const std::vector<ChunkRef>& chunks) {
   if (chunks.size() < 2) return false;

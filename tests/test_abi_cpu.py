@@ -172,22 +172,22 @@ def test_step_ex_rejects_before_enqueue(kw, expect):
 
 def test_step_ex_workspace_sizes():
     lib = mn.lib()
-    rows, cols = (3072, 1024, 12288), (12288, 3072, 3072)
+    rows, cols = (3072, 12288), (12288, 3072)   # one chunk: 2 x (3072, 12288)
     r, c = _lib.int_array(rows), _lib.int_array(cols)
-    plain = lib.muon_step_workspace_bytes(3, r, c, 0)
-    assert lib.muon_step_ex_workspace_bytes(3, r, c, 0, None) == plain
+    plain = lib.muon_step_workspace_bytes(2, r, c, 0)
+    assert lib.muon_step_ex_workspace_bytes(2, r, c, 0, None) == plain
     wd_only = _lib.MuonOptions(0.1, 1, 0, 0.0, 0.0)
-    assert lib.muon_step_ex_workspace_bytes(3, r, c, 0, ctypes.byref(wd_only)) == plain
+    assert lib.muon_step_ex_workspace_bytes(2, r, c, 0, ctypes.byref(wd_only)) == plain
     nm = _lib.MuonOptions(0.0, 1, 1, 0.9, 1e-8)
-    # NorMuon adds, for the largest group, 2 x (3072, 12288) (one wide, one
-    # tall): the per-row scales (3072 floats each) and, on the bf16 path, the
-    # last update's row sums (12288 / 64 blocks of 3072 floats each)
-    assert lib.muon_step_ex_workspace_bytes(3, r, c, 0, ctypes.byref(nm)) == (
+    # NorMuon adds, for 2 x (3072, 12288) (one wide, one tall): the per-row
+    # scales (3072 floats each) and, on the bf16 path, the last update's row
+    # sums (12288 / 64 blocks of 3072 floats each)
+    assert lib.muon_step_ex_workspace_bytes(2, r, c, 0, ctypes.byref(nm)) == (
         plain + 2 * 3072 * 4 + 2 * (12288 // 64) * 3072 * 4)
-    plain32 = lib.muon_step_workspace_bytes(3, r, c, 1)
-    assert lib.muon_step_ex_workspace_bytes(3, r, c, 1, ctypes.byref(nm)) == plain32 + 2 * 3072 * 4
+    plain32 = lib.muon_step_workspace_bytes(2, r, c, 1)
+    assert lib.muon_step_ex_workspace_bytes(2, r, c, 1, ctypes.byref(nm)) == plain32 + 2 * 3072 * 4
     bad = _lib.MuonOptions(-1.0, 1, 0, 0.0, 0.0)
-    assert lib.muon_step_ex_workspace_bytes(3, r, c, 0, ctypes.byref(bad)) == 0
+    assert lib.muon_step_ex_workspace_bytes(2, r, c, 0, ctypes.byref(bad)) == 0
     # with NorMuon the plain size is too small
     assert step_ex_call(ws_bytes=lib.muon_step_workspace_bytes(
         2, _lib.int_array((8, 16)), _lib.int_array((16, 8)), 0)) == mn.MUON_ERR_WORKSPACE
@@ -334,9 +334,18 @@ def test_small_steps_size_a_region_per_chunk():
     a = mn.orthogonalize_workspace_bytes(32, 768, 768)
     b = mn.orthogonalize_workspace_bytes(16, 768, 3072)
     assert mn.step_workspace_bytes(d768) == a + b
-    big = [(3072, 3072), (3072, 12288)] * 2
+    big = [(3072, 3072), (3072, 12288)] * 8
     assert mn.step_workspace_bytes(big) == max(
-        mn.orthogonalize_workspace_bytes(2, 3072, 3072),
-        mn.orthogonalize_workspace_bytes(2, 3072, 12288))
+        mn.orthogonalize_workspace_bytes(8, 3072, 3072),
+        mn.orthogonalize_workspace_bytes(8, 3072, 12288))
+    # the 3.8B set runs its groups in turn, the d1280 set concurrently
+    shapes = [(3072, 3072), (1024, 3072), (1024, 3072), (3072, 3072),
+              (12288, 3072), (3072, 12288)] * 28
+    assert mn.step_workspace_bytes(shapes) == mn.orthogonalize_workspace_bytes(56, 3072, 12288)
+    d1280 = ([(1280, 1280)] * 4 + [(5120, 1280), (1280, 5120)]) * 20
+    assert mn.step_workspace_bytes(d1280) == (
+        mn.orthogonalize_workspace_bytes(64, 1280, 1280)
+        + mn.orthogonalize_workspace_bytes(16, 1280, 1280)
+        + mn.orthogonalize_workspace_bytes(40, 1280, 5120))
     # one chunk: nothing to run beside it
     assert mn.step_workspace_bytes([(768, 768)] * 3) == mn.orthogonalize_workspace_bytes(3, 768, 768)
