@@ -74,6 +74,10 @@ def parse():
     p.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of a "
                         "'--steps 1 --warmup 0 --calibrate' run into profiles/traffic.json")
+    p.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
+                   help="print a markdown table of a rocprofv3 --kernel-trace CSV: the "
+                        "library's kernels by instantiation and grid, calls, average and "
+                        "total time")
     p.add_argument("--write-mfma", metavar="MFMA_CSV",
                    help="turn a rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 "
                         "SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE counter CSV of a "
@@ -200,6 +204,80 @@ def ns_flops_executed(w, compute="bf16"):
                 tot += 2.0 * tri * M                   # POLY
                 tot += 2.0 * M * N * M * cnt           # UPDATE / FINAL (full tiles)
     return tot
+
+
+_EPI_NAMES = {0: "GRAM", 1: "POLY", 2: "UPDATE", 3: "FINAL_W", 4: "FINAL_OUT", 5: "FINAL_W_T",
+              6: "FINAL_OUT_T", 7: "GRAM_LO", 8: "POLY_LO", 9: "UPDATE_ROWS"}
+
+
+def kernel_label(name):
+    """A readable label for a library kernel name as rocprofv3 prints it
+    (mangled, or demangled; its demangler renders the bf16 POLY instance as
+    '<bool _Accum, int, E, ...>')."""
+    import re
+    m = re.search(r"gemm_kernelI(DF16b|f)Li(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)"
+                  r"ELb(\d)ELb(\d)ELb(\d)E", name)
+    if m:
+        t, epi, bm, bn, wgm, wgn, st, qrow, buf, strm = m.groups()
+        flags = [x for x, on in (("rowQ", qrow), ("buf" if st == "2" else "regs", "1"),
+                                 ("stream", strm)) if on == "1"]
+        if st == "2" and buf == "0":
+            flags[flags.index("buf")] = "dma"
+        return (f"gemm<{'bf16' if t == 'DF16b' else 'fp32'},{_EPI_NAMES[int(epi)]},{bm}x{bn},"
+                f"{int(wgm) * int(wgn)}w,{','.join(flags)}>")
+    # rocprofv3's demangler garbles some bf16 instances: POLY (epilogue 1)
+    # comes out as '<bool _Accum, int, E, BM, BN, ...>', GRAM_LO (7) as
+    # '<bool _Accum, int, ELiBME, BN, ...>'
+    m = re.search(r"gemm_kernel<bool _Accum, int, E(?:Li(\d+)E)?, (\d+), (\d+), (\d+), (\d+),"
+                  r"(?: (\d+),)? (true|false), (true|false), (true|false)>", name)
+    if m:
+        lo_bm, a, b, c, d, e, qrow, buf, strm = m.groups()
+        if lo_bm:   # GRAM_LO: BM, then BN WGM WGN S
+            epi, bm, bn, wgm, wgn = "GRAM_LO", lo_bm, a, b, c
+        else:       # POLY: BM BN WGM WGN S
+            epi, bm, bn, wgm, wgn = "POLY", a, b, c, d
+        return (f"gemm<bf16,{epi},{bm}x{bn},{int(wgm) * int(wgn)}w,"
+                f"{'buf' if buf == 'true' else 'dma'}>")
+    m = re.search(r"gemm_kernel<float, (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)", name)
+    if m:
+        epi, bm, bn, wgm, wgn, st = m.groups()
+        return f"gemm<fp32,{_EPI_NAMES[int(epi)]},{bm}x{bn},{int(wgm) * int(wgn)}w,regs>"
+    m = re.search(r"prep_kernelI(DF16b|f)(DF16b|f)Lb(\d)ELb(\d)E", name)
+    if m:
+        g, x, mom, strm = m.groups()
+        return (f"prep<grad {'bf16' if g == 'DF16b' else 'fp32'},X {'bf16' if x == 'DF16b' else 'fp32'}"
+                f"{',momentum' if mom == '1' else ''}{',stream' if strm == '1' else ''}>")
+    m = re.search(r"prep_kernel<float, bool _Accum, bool, E, (true|false)>", name)
+    if m:   # the demangler's rendering of prep<fp32 grad, bf16 X, momentum>
+        return f"prep<grad fp32,X bf16,momentum{',stream' if m.group(1) == 'true' else ''}>"
+    for k in ("normuon_rowparts_kernel", "normuon_rows_kernel", "norm_kernel", "apply_kernel",
+              "prep_kernel", "gemm_kernel"):
+        if k in name:
+            garbled = "_Accum" in name or "gemm_kernel" in k or "prep_kernel" in k
+            return k.replace("_kernel", "") + (" (name garbled by the profiler's demangler)"
+                                               if garbled else "")
+    return name[:60]
+
+
+def summarize_trace(path):
+    """Markdown table of the library's kernels in a rocprofv3 kernel trace."""
+    import csv
+    agg = {}
+    for r in csv.DictReader(open(path)):
+        name = r["Kernel_Name"]
+        if not is_step_kernel(name):
+            continue
+        wg = (int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))) * int(r["Grid_Size_Y"])
+        key = (kernel_label(name), wg)
+        a = agg.setdefault(key, [0, 0])
+        a[0] += 1
+        a[1] += int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    total = sum(v[1] for v in agg.values())
+    print("| kernel | workgroups | calls | avg us | total ms | % of library time |")
+    print("|---|---|---|---|---|---|")
+    for (label, wg), (n, ns) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+        print(f"| `{label}` | {wg} | {n} | {ns / n / 1e3:.1f} | {ns / 1e6:.2f} | "
+              f"{100.0 * ns / total:.1f} |")
 
 
 def is_step_kernel(name):
@@ -430,6 +508,9 @@ def main():
     import muon_newton_schulz_step_amd as mn
     import workloads as wl
 
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
     w = wl.WORKLOADS[args.workload]
     full_count = len(w.shapes)
     if args.coeffs or args.ns_steps or args.matrices:
