@@ -200,9 +200,12 @@ int muon_step_ex(int n, const int* rows, const int* cols,
  * MUON_STATIC_SCRATCH_BYTES of device memory inside the library, one per GPU
  * (the calling thread's current device; `stream` must belong to it), held
  * from the first call on that GPU until the process ends.  The call itself
- * allocates nothing.  Shapes whose muon_step_workspace_bytes exceeds
- * MUON_STATIC_SCRATCH_BYTES return MUON_ERR_WORKSPACE before anything is
- * enqueued.  Every call on one GPU uses that GPU's one area, which keeps the
+ * allocates nothing.  It runs the step's chunks (up to 64 matrices of one
+ * oriented shape each) one after the other, never concurrently, so the area
+ * must hold the largest chunk: muon_orthogonalize_workspace_bytes of that
+ * chunk's count and oriented shape (at compute), which for a step with a
+ * single chunk is its muon_step_workspace_bytes.  A step with a larger chunk
+ * returns MUON_ERR_WORKSPACE before anything is enqueued.  Every call on one GPU uses that GPU's one area, which keeps the
  * last call's contents (the step reads none of them): calls that overlap in
  * time on one GPU (several streams, or host threads, at once) race and must
  * be serialised by the caller.  Otherwise exactly muon_step: the same checks,

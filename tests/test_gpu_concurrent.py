@@ -84,3 +84,33 @@ def test_concurrent_equals_sequential_bitwise(tmp_path):
     assert sorted(seq.files) == sorted(conc)
     for key, val in conc.items():
         assert np.array_equal(seq[key], val), key
+
+
+def test_two_streams_with_default_workspaces():
+    """Two steps at once on two streams, both with the binding's default
+    workspace: each (device, stream) gets its own, so they share no scratch
+    and each equals, bitwise, the same step run alone."""
+    announce("two streams, default workspaces")
+    w = dataclasses.replace(wl.GPT_D768, shapes=((384, 1536), (1536, 384), (384, 384)) * 4)
+    alone, together = [], []
+    for seed_shift in (0, 1):
+        ws = dataclasses.replace(w, seed=w.seed + 10 * seed_shift)
+        inp = wl.make_inputs(ws, device="cuda:0")
+        mn.step(inp["params"], inp["grads"], inp["bufs"], mu=w.mu, lr=w.lr,
+                scales=inp["scales"], coeffs=w.coeff_table, workspace=mn.Workspace())
+        torch.cuda.synchronize()
+        alone.append([p.clone() for p in inp["params"]])
+        together.append((ws, wl.make_inputs(ws, device="cuda:0")))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for (ws, inp), s in zip(together, streams):
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            mn.step(inp["params"], inp["grads"], inp["bufs"], mu=w.mu, lr=w.lr,
+                    scales=inp["scales"], coeffs=w.coeff_table)
+    torch.cuda.synchronize()
+    for a, (_, inp) in zip(alone, together):
+        for x, y in zip(a, inp["params"]):
+            assert torch.equal(x, y)
+    keys = [k for k in mn._default_ws if k[0] == "cuda:0"]
+    assert len({k[1] for k in keys}) >= 2
