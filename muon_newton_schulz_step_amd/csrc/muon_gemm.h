@@ -523,17 +523,67 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
       static_assert(PERT * NT == NCH, "staged chunks must split over the threads");
       static_assert((size_t)NCH * 16 <= (QROW ? (size_t)STAGE * 16 : LDS_BYTES), "staging fits");
       float* __restrict__ Tf = QROW ? reinterpret_cast<float*>(S0) : reinterpret_cast<float*>(smem);
+      // bf16 path: the block's X state (its SR rows, all BN columns) arrives
+      // as 16-byte runs of 8 columns of hi and lo, coalesced, and waits in
+      // the other stage as fp32 rows (columns of rows with bit 2 set XOR 32,
+      // so the two half-waves' reads below hit different banks); the next
+      // block's runs are loaded during this block's write-back.
+      constexpr int RPR = BN / 8;         // runs per X row of the block
+      constexpr int RPT = SR * RPR / NT;  // runs per thread and block
+      static_assert(!HILO || (QROW && RPT * NT == SR * RPR &&
+                              (size_t)SR * BN * 4 <= (size_t)STAGE * 16 && BN % 64 == 0),
+                    "the block's X state fits in a stage");
+      float* __restrict__ Xs = reinterpret_cast<float*>(S1);
+      auto xs_at = [](int il, int jl) __attribute__((always_inline)) {
+        return il * BN + (jl ^ (((il >> 2) & 1) << 5));
+      };
+      [[maybe_unused]] u32x4_t hv[HILO ? RPT : 1], lv[HILO ? RPT : 1];
+      auto xload = [&](int mi) __attribute__((always_inline)) {
+#pragma unroll
+        for (int s = 0; s < RPT; ++s) {
+          const int u = tid + NT * s, il = u / RPR, jr = u % RPR;
+          const long long o =
+              (long long)(ti * BM + (il / 32) * WTM + mi * 32 + il % 32) * a.ldx + tj * BN + 8 * jr;
+          hv[s] = ldx(reinterpret_cast<const u32x4_t*>(Xh + o));
+          lv[s] = ldx(reinterpret_cast<const u32x4_t*>(Xl + o));
+        }
+      };
+      auto xstore = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int s = 0; s < RPT; ++s) {
+          const int u = tid + NT * s, il = u / RPR, jr = u % RPR;
+          float x[8];
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const unsigned hw = hv[s][w], lw = lv[s][w];
+            x[2 * w] = __uint_as_float(hw << 16) + __uint_as_float(lw << 16);
+            x[2 * w + 1] = __uint_as_float(hw & 0xffff0000u) + __uint_as_float(lw & 0xffff0000u);
+          }
+          float* d = Xs + xs_at(il, 8 * jr);
+          *reinterpret_cast<f32x4_t*>(d) = f32x4_t{x[0], x[1], x[2], x[3]};
+          *reinterpret_cast<f32x4_t*>(d + 4) = f32x4_t{x[4], x[5], x[6], x[7]};
+        }
+      };
+      if constexpr (HILO) xload(0);
       static_for<FM>([&](auto mi) {
-        const int ib = i_base + mi * 32 + 4 * hsel;  // + 8q + t
+        if constexpr (HILO) {
+          xstore();
+          if constexpr (decltype(mi)::value + 1 < FM) xload(decltype(mi)::value + 1);
+          __syncthreads();
+        }
+        [[maybe_unused]] const int ib = i_base + mi * 32 + 4 * hsel;  // + 8q + t
         static_for<FN>([&](auto ni) {
-          const int j = j_base + ni * 32 + (lane & 31);
+          [[maybe_unused]] const int j = j_base + ni * 32 + (lane & 31);
+          const int jl = jl0 + ni * 32;
           float ein[16];
           static_for<16>([&](auto r) {
-            const long long o = (long long)(ib + 8 * (r / 4) + (r % 4)) * a.ldx + j;
-            if constexpr (HILO) ein[r] = to_f32(ldx(Xh + o)) + to_f32(ldx(Xl + o));
-            else ein[r] = Xf[o];
+            if constexpr (HILO) {
+              ein[r] = Xs[xs_at(wm * 32 + 8 * (r / 4) + 4 * hsel + r % 4, jl)];
+            } else {
+              const long long o = (long long)(ib + 8 * (r / 4) + (r % 4)) * a.ldx + j;
+              ein[r] = Xf[o];
+            }
           });
-          const int jl = jl0 + ni * 32;
           static_for<4>([&](auto q) {
             f32x4_t f;
             static_for<4>([&](auto t) {
