@@ -497,6 +497,39 @@ def measure_peaks(torch, mn, dev):
                    "flight per thread (10 launches each at 1024-8192 workgroups, the best)"}
 
 
+def measure_vendor_gemm(torch, dev, w):
+    """The vendor's bf16 GEMM (torch.bmm / torch.mm, hipBLASLt underneath) on
+    the workload's largest update product, B (M x M) times X (M x N) batched
+    over the group (at most 56 matrices), and on one 8192^3 product: what a
+    tuned library reaches on these shapes on this GPU, beside the step's own
+    kernels.  Contiguous operands only."""
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    groups = w.oriented_groups()
+    (m, n), cnt = max(groups.items(), key=lambda kv: kv[0][0] ** 2 * kv[0][1] * kv[1])
+    cnt = min(cnt, 56)
+    out = {}
+    for key, (a_shape, b_shape, fl) in {
+            f"bmm_{cnt}x{m}x{m}_by_{m}x{n}": ((cnt, m, m), (cnt, m, n), 2.0 * cnt * m * m * n),
+            "mm_8192x8192x8192": ((8192, 8192), (8192, 8192), 2.0 * 8192 ** 3)}.items():
+        g = torch.Generator(device=dev).manual_seed(0)
+        a = torch.randn(a_shape, generator=g, device=dev, dtype=torch.bfloat16)
+        b = torch.randn(b_shape, generator=g, device=dev, dtype=torch.bfloat16)
+        mul = torch.bmm if a.dim() == 3 else torch.mm
+        c = mul(a, b)  # warm-up (and the library's kernel choice)
+        reps = 5
+        e0.record(stream)
+        for _ in range(reps):
+            mul(a, b, out=c)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[key + "_tflops"] = round(fl * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+        del a, b, c
+    out["how"] = ("torch.bmm / torch.mm in bf16 on contiguous random operands, 5 calls after "
+                  "one warm-up call, HIP events on the current stream")
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -563,7 +596,9 @@ def main():
     gc.collect()
     gc.disable()
     stream = torch.cuda.current_stream(dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # an event after every step: the whole region (first to last) gives the
+    # mean, the gaps between them the median and the minimum
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     mn.timing_enable(False)
     if args.graph:
         # the workspace was allocated by the warm-up steps: capture allocates nothing
@@ -572,19 +607,22 @@ def main():
             one_step()
         graph.replay()
         torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(args.steps):
+        ev[0].record(stream)
+        for i in range(args.steps):
             graph.replay()
-        e1.record(stream)
+            ev[i + 1].record(stream)
         torch.cuda.synchronize()
         del graph
     else:
-        e0.record(stream)
-        for _ in range(args.steps):
+        ev[0].record(stream)
+        for i in range(args.steps):
             one_step()
-        e1.record(stream)
+            ev[i + 1].record(stream)
         torch.cuda.synchronize()
-    ms_per_step = e0.elapsed_time(e1) / args.steps
+    ms_per_step = ev[0].elapsed_time(ev[-1]) / args.steps
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+    ms_median = per_step[len(per_step) // 2] if len(per_step) % 2 else \
+        0.5 * (per_step[len(per_step) // 2 - 1] + per_step[len(per_step) // 2])
     # the per-kernel pass: the same steps again, each launch between events
     mn.timing_enable(True)
     mn.timing_read()
@@ -596,6 +634,8 @@ def main():
     records = mn.timing_read()
     kernels = kernel_summary(records, args.steps)
     peaks = None if args.no_peaks else measure_peaks(torch, mn, dev)
+    if peaks is not None and args.compute == "bf16":
+        peaks["vendor_gemm"] = measure_vendor_gemm(torch, dev, w)
     ns = [k for k in kernels if k["kind"] in ("gram", "gramq", "poly", "update", "final")]
     ns_ms = sum(k["ms"] for k in ns) / args.steps
     flops = w.ns_flops_counted()
@@ -626,6 +666,26 @@ def main():
     roof["avg_launch_ms"] = round(dom["avg_launch_ms"], 4)
     roof["traffic"] = traffic_from_profiles(dom_key)
 
+    # element-wise part: the optimizer state's own bytes per element (gradient
+    # read, momentum read and written, weights read and written); prep moves
+    # the first three (and writes X_0), the weights move in the FINAL epilogue
+    elements = sum(r * c for r, c in w.shapes)
+    gbytes = 2 if w.grad_dtype == torch.bfloat16 else 4
+    preps = [k for k in kernels if k["kind"] in ("prep", "norm")]
+    prep_ms = sum(k["ms"] for k in preps) / args.steps
+    prep_moved = sum(k["bytes"] for k in preps) / args.steps
+    elementwise = {
+        "algorithmic_bytes_per_element": gbytes + 16, "elements": elements,
+        "prep_norm_ms_per_step": round(prep_ms, 4),
+        "prep_gbs_moved": round(prep_moved / (prep_ms * 1e-3) / 1e9, 1) if prep_ms > 0 else None,
+        "prep_frac_of_hbm_peak": round(prep_moved / (prep_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        if prep_ms > 0 else None,
+        "note": "weights are read and written inside the last update's epilogue, whose "
+                "time is not separable from its GEMM"}
+    if peaks and prep_ms > 0:
+        elementwise["prep_frac_of_measured_copy"] = round(
+            prep_moved / (prep_ms * 1e-3) / 1e9 / peaks["copy_gbs"], 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_sample_seconds, args.variant)
@@ -639,6 +699,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 3),
+        "ms_per_step_median": round(ms_median, 3),
+        "ms_per_step_min": round(per_step[0], 3),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
@@ -662,6 +724,7 @@ def main():
         "ns_frac_of_peak_executed": round(exec_flops / (ns_ms * 1e-3) / 1e12 / PEAK[args.compute],
                                           4),
         "measured_peaks": peaks,
+        "elementwise": elementwise,
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": [{k2: (round(v, 4) if isinstance(v, float) else v) for k2, v in k.items()

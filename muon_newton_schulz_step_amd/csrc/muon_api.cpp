@@ -95,11 +95,20 @@ bool gram_by_qaq(bool cbf16, long long M, long long N) { return cbf16 && N >= 4 
 // over more than one step.
 bool qaq_step(int k, int n_steps) { return (k == 1 || k == 3) && k <= n_steps - 2; }
 
-// Chunks whose X state is larger than the chip's 256 MB last-level cache
-// stream it: the UPDATE / FINAL epilogues and prep load and store the X
-// state, weights, gradient and momentum nontemporally, which leaves L2 to
-// the GEMM operand panels.  Smaller ones keep X cached for the next launch.
+// When the X state resident at one time (the chunk's own, or the sum over
+// the chunks of a step that runs them concurrently) is larger than the
+// chip's 256 MB last-level cache, the chunks stream it: the UPDATE / FINAL
+// epilogues and prep load and store the X state, weights, gradient and
+// momentum nontemporally, which leaves L2 to the GEMM operand panels.
+// Smaller ones keep X cached for the next launch.  (The d768 GPT set, two
+// concurrent chunks of 113 and 226 MB: 1.67 ms cached, 1.57 ms streamed.)
 constexpr double kStreamBytes = 256.0 * (1 << 20);
+
+// X-state bytes of a chunk of `cnt` matrices of oriented shape m x n:
+// bf16 hi twice + lo, fp32 X + X^T twice.
+double x_state_bytes(int cnt, int m, int n, bool cbf16) {
+  return (double)cnt * (double)pad_dim(m) * (double)pad_dim(n) * (cbf16 ? 6.0 : 12.0);
+}
 
 bool make_layout(int cnt, int m, int n, bool cbf16, Layout& L, bool normuon = false) {
   const long long M = pad_dim(m), N = pad_dim(n);
@@ -208,8 +217,10 @@ struct Chunk {
   RowTable vt;                        // NorMuon second moments
 };
 
+// resident_x: the X-state bytes resident while this chunk runs (its own, or
+// those of every chunk running concurrently with it).
 int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeffs, int n_steps,
-              float eps, bool cbf16, hipStream_t s) {
+              float eps, bool cbf16, double resident_x, hipStream_t s) {
   const size_t es = cbf16 ? 2 : 4;
   const long long MN = (long long)L.M * L.N, MM = (long long)L.M * L.M;
   // bf16: Xh[2] (hi planes), Xl; fp32: Xf, XT[2]
@@ -227,9 +238,7 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
   const double elems = m * n * cnt;
   const double pmn = cnt * (double)MN, pmm = cnt * (double)MM;  // padded elements
 
-  // X state: hi twice + lo (bf16), or X + X^T twice (fp32)
-  const bool stream =
-      stream_pref() >= 0 ? stream_pref() == 1 : pmn * (cbf16 ? 6.0 : 12.0) > kStreamBytes;
+  const bool stream = stream_pref() >= 0 ? stream_pref() == 1 : resident_x > kStreamBytes;
   PrepArgs pa{};
   pa.m = L.m; pa.n = L.n; pa.M = L.M; pa.N = L.N;
   pa.stream = stream;
@@ -372,22 +381,32 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
       });
     } else {
       // The chunk holds its wide matrices first, then the tall ones, which
-      // store the result transposed; each part has its own launch.
+      // store the result transposed; each part has its own launch, its tile
+      // size chosen for its own count.  When both parts are too small for
+      // 256 x 256 tiles, the bf16 weight update takes them in one launch of
+      // 128 x 128 tiles instead (the kernel branches per matrix), so that
+      // they share their rounds of tiles.
       const int ntall = __builtin_popcountll(c.tall_mask);
       const int nwide = c.cnt - ntall;
-      for (int part = 0; part < 2 && err == hipSuccess; ++part) {
-        const int b = part == 0 ? nwide : ntall;
+      const long long t256_mat = (long long)t256 * (L.N / 256);
+      const bool mix = cbf16 && c.final_mode == FINAL_WEIGHTS && nwide > 0 && ntall > 0 &&
+                       pick_tile(cbf16, t256_mat, nwide > ntall ? nwide : ntall) == 128;
+      for (int part = 0; part < (mix ? 1 : 2) && err == hipSuccess; ++part) {
+        const int b = mix ? c.cnt : part == 0 ? nwide : ntall;
         if (b == 0) continue;
         GemmArgs gf = g;
         gf.mat0 = part == 0 ? 0 : nwide;
-        const int epi = c.final_mode == FINAL_WEIGHTS ? (part ? EPI_FINAL_W_T : EPI_FINAL_W)
-                                                      : (part ? EPI_FINAL_OUT_T : EPI_FINAL_OUT);
+        const int tile_f = mix ? 128 : pick_tile(cbf16, t256_mat, b);
+        gf.tiles_m = L.M / tile_f; gf.tiles_n = L.N / tile_f;
+        const int epi = mix ? EPI_FINAL_W_MIX
+                        : c.final_mode == FINAL_WEIGHTS ? (part ? EPI_FINAL_W_T : EPI_FINAL_W)
+                                                        : (part ? EPI_FINAL_OUT_T : EPI_FINAL_OUT);
         const double bm = b, pmn_b = bm * (double)MN, el_b = m * n * bm;
         const double fin_bytes = bm * (double)MM * es + pmn_b * es + pmn_b * 4.0 +
                                  (c.final_mode == FINAL_WEIGHTS ? el_b * 8.0
                                                                 : el_b * (c.out_bf16 ? 2.0 : 4.0));
         err = timed(MUON_K_FINAL, L.m, L.n, b, k, bm * 2.0 * m * m * n, bm * x_upd, fin_bytes, s,
-                    [&] { return launch_gemm(cbf16, epi, tile_upd, gf, c.wt, b, s); });
+                    [&] { return launch_gemm(cbf16, epi, tile_f, gf, c.wt, b, s); });
       }
     }
     if (err != hipSuccess) return MUON_ERR_HIP;
@@ -632,6 +651,9 @@ int step_impl(int n, const int* rows, const int* cols, void* const* params, int 
   std::vector<ChunkRef> chunks;
   list_chunks(groups, chunks);
   char* ws = static_cast<char*>(workspace);
+  double resident_all = 0.0;
+  for (const ChunkRef& r : chunks)
+    resident_all += x_state_bytes(r.cnt, groups[r.g].m, groups[r.g].n, cbf16);
 
   // Concurrent chunks: lane 0 is the caller's stream, the others fork off it
   // and are joined back to it at the end (also after a failed launch, so
@@ -691,7 +713,9 @@ int step_impl(int n, const int* rows, const int* cols, void* const* params, int 
       c.beta2 = opt->beta2;
       c.eps2 = opt->normuon_eps;
     }
-    status = run_chunk(c, L, ws + ws_off[ci], coeffs, n_steps, eps, cbf16, lane[ci % nlanes]);
+    const double resident = conc ? resident_all : x_state_bytes(cnt, g.m, g.n, cbf16);
+    status = run_chunk(c, L, ws + ws_off[ci], coeffs, n_steps, eps, cbf16, resident,
+                       lane[ci % nlanes]);
   }
   for (int l = 1; l < nlanes; ++l) {
     if (hipEventRecord(lanes->join[l - 1], lane[l]) != hipSuccess ||
@@ -812,7 +836,9 @@ int muon_orthogonalize(const void* in, int in_dtype, void* out, int out_dtype, i
     c.out = static_cast<char*>(out) + (size_t)b0 * batch_stride * osz;
     c.s_out = batch_stride;
     c.out_bf16 = out_dtype == MUON_BF16;
-    if (int st = run_chunk(c, L, ws, coeffs, n_steps, eps, cbf16, stream)) return st;
+    if (int st = run_chunk(c, L, ws, coeffs, n_steps, eps, cbf16,
+                           x_state_bytes(cnt, m, n, cbf16), stream))
+      return st;
   }
   return MUON_OK;
 }

@@ -211,16 +211,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
   constexpr size_t MAIN_BYTES = 2 * (size_t)STAGE * 16;
   constexpr size_t EPI_BYTES = (size_t)BN * TLD * sizeof(T);
   constexpr size_t LDS_BYTES = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
-  constexpr bool FIN_W = EPI == EPI_FINAL_W || EPI == EPI_FINAL_W_T;
+  constexpr bool FIN_W = EPI == EPI_FINAL_W || EPI == EPI_FINAL_W_T || EPI == EPI_FINAL_W_MIX;
   constexpr bool FIN_OUT = EPI == EPI_FINAL_OUT || EPI == EPI_FINAL_OUT_T;
   constexpr bool FINAL = FIN_W || FIN_OUT;
   constexpr bool TALLF = EPI == EPI_FINAL_W_T || EPI == EPI_FINAL_OUT_T;  // FINAL, tall matrices
+  constexpr bool MIXF = EPI == EPI_FINAL_W_MIX;  // FINAL, the orientation per matrix
   constexpr bool HILO = sizeof(T) == 2;  // bf16 path: X state as hi + lo planes
   constexpr bool GRAMK = EPI == EPI_GRAM || EPI == EPI_GRAM_LO;
   constexpr bool POLYK = EPI == EPI_POLY || EPI == EPI_POLY_LO;
   constexpr bool UPD = EPI == EPI_UPDATE || EPI == EPI_UPDATE_ROWS;
   constexpr bool ROWS = EPI == EPI_UPDATE_ROWS;
   static_assert(!ROWS || HILO, "row sums on the bf16 path");
+  static_assert(!MIXF || HILO, "mixed orientations on the bf16 path");
   constexpr bool STAGED_T = GRAMK || POLYK || (UPD && !HILO);
   static_assert(FM * 32 * WGM == BM && FN * 32 * WGN == BN, "wave tiles must be 32-aligned");
   static_assert(S == 0 || S == 2, "main loop variants");
@@ -513,9 +515,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
   // contiguous in memory but neighbouring lanes are a row of W apart.  Each
   // 32-row block of every wave goes through LDS instead, as [j][i] rows of
   // 16-byte chunks (chunk c of row j at slot c ^ (j % SCH)), and the block
-  // then updates whole 16-byte runs of W's rows, coalesced.
-  if constexpr (TALLF) {
-    {
+  // then updates whole 16-byte runs of W's rows, coalesced.  (MIXF: a
+  // workgroup-uniform branch on its matrix's orientation.)
+  if constexpr (TALLF || MIXF) {
+    if (TALLF || ((a.tall_mask >> mat) & 1ull)) {
       constexpr int SR = 32 * WGM;  // staged i per j row
       constexpr int SCH = SR / 4;   // 16-byte chunks per staged row
       constexpr int NCH = BN * SCH;
@@ -982,7 +985,7 @@ inline bool buffer_loads(int epi) {
   }();
   if (v >= 0) return v == 1;
   return !(epi == EPI_FINAL_W || epi == EPI_FINAL_OUT || epi == EPI_FINAL_W_T ||
-           epi == EPI_FINAL_OUT_T);
+           epi == EPI_FINAL_OUT_T || epi == EPI_FINAL_W_MIX);
 }
 
 template <typename T, int E>
@@ -998,21 +1001,25 @@ inline void launch_gemm_t(int tile, const GemmArgs& a, const WeightTable& t, dim
     const bool buf = buffer_loads(E) && (long long)tile * ld * (long long)sizeof(T) < (1LL << 31);
     auto go = [&](auto strm) {
       constexpr bool ST = decltype(strm)::value;
-      if (tile == 256) {
-        if (buf)
-          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 2, QR, true, ST>), grid,
-                             dim3(512), 0, s, launch);
-        else
-          hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 2, QR, false, ST>), grid,
-                             dim3(512), 0, s, launch);
-      } else {
-        if (buf)
-          hipLaunchKernelGGL((gemm_kernel<T, E, 128, 128, 2, 2, 2, QR, true, ST>), grid,
-                             dim3(256), 0, s, launch);
-        else
-          hipLaunchKernelGGL((gemm_kernel<T, E, 128, 128, 2, 2, 2, QR, false, ST>), grid,
-                             dim3(256), 0, s, launch);
+      // the mixed-orientation FINAL exists as 128 x 128 tiles only (with both
+      // epilogues in one kernel the 256 x 256 tile runs out of registers)
+      if constexpr (E != EPI_FINAL_W_MIX) {
+        if (tile == 256) {
+          if (buf)
+            hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 2, QR, true, ST>), grid,
+                               dim3(512), 0, s, launch);
+          else
+            hipLaunchKernelGGL((gemm_kernel<T, E, 256, 256, 2, 4, 2, QR, false, ST>), grid,
+                               dim3(512), 0, s, launch);
+          return;
+        }
       }
+      if (buf)
+        hipLaunchKernelGGL((gemm_kernel<T, E, 128, 128, 2, 2, 2, QR, true, ST>), grid,
+                           dim3(256), 0, s, launch);
+      else
+        hipLaunchKernelGGL((gemm_kernel<T, E, 128, 128, 2, 2, 2, QR, false, ST>), grid,
+                           dim3(256), 0, s, launch);
     };
     // streaming accesses exist only in the row-major-X (UPDATE / FINAL) epilogues
     if (QR && a.stream)

@@ -26,7 +26,9 @@ enum Epi {
   EPI_FINAL_W_T = 5, EPI_FINAL_OUT_T = 6,
   EPI_GRAM_LO = 7,  // bf16 GRAM that also writes C's residual to Clo
   EPI_POLY_LO = 8,  // bf16 POLY whose A input is Ain + Alo
-  EPI_UPDATE_ROWS = 9  // bf16 UPDATE that also writes row sums of the new X^2
+  EPI_UPDATE_ROWS = 9,  // bf16 UPDATE that also writes row sums of the new X^2
+  EPI_FINAL_W_MIX = 10  // bf16 FINAL_W over wide and tall matrices in one launch,
+                        // each matrix's orientation from tall_mask
 };
 enum Final { FINAL_NONE = 0, FINAL_OUT = 1, FINAL_WEIGHTS = 2 };
 

@@ -349,7 +349,7 @@ hipError_t launch_gemm(int compute_bf16, int epi, int tile, const GemmArgs& a_in
     launch_gemm_poly(epi, tile, a, t, grid, s);
   } else if (epi == EPI_UPDATE || epi == EPI_UPDATE_ROWS) {
     launch_gemm_update(epi, tile, a, t, grid, s);
-  } else if (epi == EPI_FINAL_W || epi == EPI_FINAL_W_T) {
+  } else if (epi == EPI_FINAL_W || epi == EPI_FINAL_W_T || epi == EPI_FINAL_W_MIX) {
     launch_gemm_final_w(epi, tile, a, t, grid, s);
   } else {
     launch_gemm_final_out(epi, tile, a, t, grid, s);
