@@ -54,6 +54,19 @@ def test_step_mixed_shapes(compute, grad_dtype):
         check_matrix(w, inputs, k, before, bufs_before, compute)
 
 
+def test_step_final_parts_with_their_own_tiles():
+    """One oriented chunk of 32 wide 512x2048 matrices and one tall 2048x512:
+    the wide part's weight update runs on 256x256 tiles (512 of them), the
+    tall part's alone on 128x128 tiles."""
+    announce("step final parts, different tiles")
+    shapes = ((512, 2048),) * 32 + ((2048, 512),)
+    w = dataclasses.replace(wl.GPT_D768, shapes=shapes)
+    inputs = wl.make_inputs(w, device=DEV)
+    before, bufs_before = run_step(w, inputs, "bf16")
+    for k in (0, 17, 31, 32):
+        check_matrix(w, inputs, k, before, bufs_before, "bf16", tiles=True)
+
+
 @pytest.mark.parametrize("compute", ["bf16", "fp32"])
 def test_single_256x128_workload(compute):
     announce("single 256x128", compute)
