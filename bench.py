@@ -152,7 +152,8 @@ def launch_sequence(w):
     per oriented group (first appearance) and chunk of at most 64 matrices,
     prep, norm, then gram, poly, update per Newton-Schulz step, the last
     update being one final launch for the chunk's wide matrices and one for
-    its tall ones.  Groups with padded N >= 4M and M >= 2048 form the Gram
+    its tall ones (a single one for both when neither part alone fills 512
+    tiles of 256 x 256).  Groups with padded N >= 4M and M >= 2048 form the Gram
     matrix of steps 1 and 3 (not the last) in two gramq launches instead."""
     def pad(d):
         return (d + 255) // 256 * 256
@@ -164,7 +165,11 @@ def launch_sequence(w):
         qaq = pad(n) >= 4 * pad(m) and pad(m) >= 2048
         for b0 in range(0, len(talls), 64):
             chunk = talls[b0:b0 + 64]
-            finals = [("final", m, n)] * ((not all(chunk)) + any(chunk))
+            nt = sum(chunk)
+            nw = len(chunk) - nt
+            # one launch for both parts when neither fills 512 tiles of 256 x 256
+            mixed = nw > 0 and nt > 0 and max(nw, nt) * (pad(m) // 256) * (pad(n) // 256) < 512
+            finals = [("final", m, n)] * (1 if mixed else (nw > 0) + (nt > 0))
             seq += [("prep", m, n), ("norm", m, n)]
             for k in range(w.n_steps):
                 if qaq and k in (1, 3) and k <= w.n_steps - 2:
@@ -207,7 +212,7 @@ def ns_flops_executed(w, compute="bf16"):
 
 
 _EPI_NAMES = {0: "GRAM", 1: "POLY", 2: "UPDATE", 3: "FINAL_W", 4: "FINAL_OUT", 5: "FINAL_W_T",
-              6: "FINAL_OUT_T", 7: "GRAM_LO", 8: "POLY_LO", 9: "UPDATE_ROWS"}
+              6: "FINAL_OUT_T", 7: "GRAM_LO", 8: "POLY_LO", 9: "UPDATE_ROWS", 10: "FINAL_W_MIX"}
 
 
 def kernel_label(name):
