@@ -2,7 +2,10 @@
 on the caller's stream (no allocation, memset or synchronisation), so a
 captured step replays as a graph.  Each replay must equal the same step run
 eagerly, bitwise (the kernels are deterministic); replays reuse the captured
-arguments (lr, mu, scales, coefficients)."""
+arguments (lr, mu, scales, coefficients).  Two sets: small chunks that run
+concurrently on library lanes (forked off the captured stream and joined
+back to it), and a large chunk beside a small one, which run in turn on the
+captured stream."""
 import dataclasses
 
 import pytest
@@ -16,11 +19,19 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
+SETS = {
+    "concurrent": ((96, 256), (256, 96), (128, 128), (300, 700), (768, 768)),
+    # 2 x 4096 x 16384 is a large chunk (2 x 4096^2 x 16384 multiply-adds per
+    # update), so the step runs its two chunks in turn
+    "in_turn": ((4096, 16384), (16384, 4096), (256, 512)),
+}
+
+
 @pytest.mark.parametrize("compute", ["bf16", "fp32"])
-def test_captured_step_replays_match_eager(compute):
-    announce("graph capture", compute)
-    w = dataclasses.replace(wl.GPT_D768, shapes=((96, 256), (256, 96), (128, 128), (300, 700),
-                                                 (768, 768)))
+@pytest.mark.parametrize("which", sorted(SETS))
+def test_captured_step_replays_match_eager(compute, which):
+    announce("graph capture", compute, which)
+    w = dataclasses.replace(wl.GPT_D768, shapes=SETS[which])
     a = wl.make_inputs(w, device=DEV)  # replayed
     b = wl.make_inputs(w, device=DEV)  # eager, same seeded values
     need = mn.step_workspace_bytes(w.shapes, compute)
