@@ -16,6 +16,21 @@ BUF_TOL = 1e-6    # momentum buffer, fp32 arithmetic vs fp64
 # the emulated maximum stays below 2e-2 (64x64: 1.8e-2, 128x128: 1.5e-2).
 BF16_SMALL_TOL = {(1, 1): 0.15, (1, 5): 0.11, (2, 8): 0.14, (5, 5): 0.09, (8, 16): 0.048}
 SMALL_DIM = 64
+# bf16 path on degenerate inputs (workloads.degenerate_matrix) whose
+# singular vectors are flat: the bf16 rounding of B is then the same in many
+# entries and adds up instead of averaging out.  A kind keeps BF16_TOL when
+# the emulated bf16 path stays within 0.8 BF16_TOL on the shapes the GPU test
+# uses (DEGENERATE_SHAPES); otherwise its bound lies between 1.1 and 1.25
+# times the emulated maximum (tests/test_bf16_emulation.py checks both:
+# constant 2.10e-2, duplicated rows 1.91e-2).
+DEGENERATE_SHAPES = ((256, 384), (384, 256), (1024, 3072))
+DEGENERATE_BF16_TOL = {"constant": 2.6e-2, "dup_rows": 2.3e-2}
+
+
+def degenerate_tol(kind, compute):
+    if compute != "bf16":
+        return FP32_TOL
+    return DEGENERATE_BF16_TOL.get(kind, BF16_TOL)
 
 
 def tol(compute, shape=None):

@@ -23,7 +23,9 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_helpers import BF16_SMALL_TOL, BF16_TOL, SMALL_DIM
+import workloads as wl
+from gpu_helpers import (BF16_SMALL_TOL, BF16_TOL, DEGENERATE_BF16_TOL, DEGENERATE_SHAPES,
+                         SMALL_DIM)
 
 Q5 = [(3.4445, -4.7750, 2.0315)] * 5
 
@@ -134,6 +136,26 @@ def test_from_64_rows_on_the_plain_bar_holds(shape):
     assert min(shape) >= SMALL_DIM
     e = emulated_errors(shape, 100, SEED)
     assert e.max() <= 0.95 * BF16_TOL, e.max()
+
+
+# ------------------------------- degenerate inputs, bounds derived
+@pytest.mark.parametrize("kind", wl.DEGENERATE_KINDS)
+def test_degenerate_bounds_are_derived(kind):
+    """A degenerate kind keeps the plain bar when the emulated bf16 path stays
+    within 0.8 of it on every shape the GPU test uses; otherwise its bound is
+    between 1.1 and 1.25 times the emulated maximum."""
+    e = []
+    for shape in DEGENERATE_SHAPES:
+        x = wl.degenerate_matrix(kind, *shape).numpy()
+        ref = oracle.orthogonalize(x.astype(np.float64), Q5)
+        e.append(oracle.relative_frobenius_error(emulate(x, Q5), ref))
+    worst = max(e)
+    print(kind, ["%.3e" % v for v in e])
+    if kind in DEGENERATE_BF16_TOL:
+        assert worst > 0.8 * BF16_TOL
+        assert 1.1 * worst <= DEGENERATE_BF16_TOL[kind] <= 1.25 * worst
+    else:
+        assert worst <= 0.8 * BF16_TOL
 
 
 # -------------------------------------------- the two design choices

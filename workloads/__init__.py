@@ -247,3 +247,40 @@ def gaussian_batch(batch: int, rows: int, cols: int, seed: int, device="cpu",
     return torch.stack([
         _randn((rows, cols), _gen(device, seed, i, _AUX), device, std)
         for i in range(batch)]).to(dtype)
+
+
+# Degenerate inputs for the edge-case parity tests: each a seeded fp32 matrix
+# made on the host (numpy's PCG64), so that the GPU test and the CPU-side
+# bf16 emulation see the same values.
+DEGENERATE_KINDS = ("rank1", "one_element", "zero_rows", "dup_rows", "constant",
+                    "col_scales", "row_scales")
+
+
+def degenerate_matrix(kind: str, rows: int, cols: int, seed: int = 7,
+                      device="cpu") -> torch.Tensor:
+    """rank1: an outer product of two Gaussian vectors; one_element: a single
+    non-zero entry; zero_rows: Gaussian with every other row zero; dup_rows:
+    8 Gaussian rows, each repeated rows/8 times (rank 8); constant: all ones;
+    col_scales / row_scales: Gaussian with columns / rows scaled by 10^u, u
+    uniform in [-3, 3] (singular values spread over six decades)."""
+    import numpy as np
+    rng = np.random.default_rng([seed, DEGENERATE_KINDS.index(kind)])
+    if kind == "rank1":
+        x = np.outer(rng.standard_normal(rows), rng.standard_normal(cols))
+    elif kind == "one_element":
+        x = np.zeros((rows, cols))
+        x[int(rng.integers(rows)), int(rng.integers(cols))] = -3.3  # not a bf16 value
+    elif kind == "zero_rows":
+        x = rng.standard_normal((rows, cols)) * (np.arange(rows)[:, None] % 2)
+    elif kind == "dup_rows":
+        assert rows % 8 == 0
+        x = np.repeat(rng.standard_normal((8, cols)), rows // 8, axis=0)
+    elif kind == "constant":
+        x = np.ones((rows, cols))
+    elif kind == "col_scales":
+        x = rng.standard_normal((rows, cols)) * (10.0 ** rng.uniform(-3, 3, cols))[None, :]
+    elif kind == "row_scales":
+        x = rng.standard_normal((rows, cols)) * (10.0 ** rng.uniform(-3, 3, rows))[:, None]
+    else:
+        raise ValueError(kind)
+    return torch.from_numpy(x.astype(np.float32)).to(device)
