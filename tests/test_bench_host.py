@@ -1,0 +1,61 @@
+"""Host-side logic of bench.py, on the CPU: the refusal of several GPUs,
+the launch-sequence model the counter summaries are matched against, the
+executed-flop count, and the labels given to kernel names."""
+import os
+import subprocess
+import sys
+
+import bench
+import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    out = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert out.returncode == 2
+    assert "one GPU" in out.stderr and out.stdout == ""
+
+
+def test_launch_sequence_of_the_3p8b_step():
+    seq = bench.launch_sequence(wl.GPT_3P8B)
+    groups = {}
+    for kind, m, n in seq:
+        groups.setdefault((m, n), []).append(kind)
+    assert list(groups) == [(3072, 3072), (1024, 3072), (3072, 12288)]
+    # square and wide groups: prep, norm, 5 x (gram, poly), 4 updates, 1 final
+    for key in ((3072, 3072), (1024, 3072)):
+        g = groups[key]
+        assert g[:2] == ["prep", "norm"] and g.count("gram") == 5 and g.count("poly") == 5
+        assert g.count("update") == 4 and g.count("final") == 1 and len(g) == 17
+    # the 3072 x 12288 group: the Gram matrix of steps 1 and 3 formed as
+    # Q A Q (two launches counted as gramq each), one final per orientation
+    # (28 + 28, each part alone fills 512 tiles of 256 x 256)
+    g = groups[(3072, 12288)]
+    assert g.count("gram") == 3 and g.count("gramq") == 4 and g.count("poly") == 5
+    assert g.count("update") == 4 and g.count("final") == 2
+
+
+def test_launch_sequence_mixed_final_when_parts_are_small():
+    # d768: the (768, 3072) chunk holds 8 wide and 8 tall matrices, 36 tiles
+    # of 256 x 256 each: one final launch for both
+    seq = bench.launch_sequence(wl.GPT_D768)
+    finals = [(m, n) for kind, m, n in seq if kind == "final"]
+    assert finals == [(768, 768), (768, 3072)]
+
+
+def test_executed_flops_of_the_3p8b_step():
+    # the figure the MFMA counters measured on the GPU (profiles/mfma.json)
+    assert bench.ns_flops_executed(wl.GPT_3P8B) == 139004469051392.0
+    # counted: the method's 4 m^2 n + 2 m^3 per matrix and step
+    assert abs(wl.GPT_3P8B.ns_flops_counted() - 1.99029e14) < 1e9
+
+
+def test_kernel_labels():
+    name = "void muon::gemm_kernel<__bf16, 2, 256, 256, 2, 4, 2, true, true, true>(muon::GemmLaunch)"
+    mangled = "_ZN4muon11gemm_kernelIDF16bLi2ELi256ELi256ELi2ELi4ELi2ELb1ELb1ELb1EEEvNS_10GemmLaunchE"
+    assert bench.kernel_label(mangled) == "gemm<bf16,UPDATE,256x256,8w,rowQ,buf,stream>"
+    mixed = "_ZN4muon11gemm_kernelIDF16bLi10ELi128ELi128ELi2ELi2ELi2ELb1ELb0ELb1EEEvNS_10GemmLaunchE"
+    assert bench.kernel_label(mixed) == "gemm<bf16,FINAL_W_MIX,128x128,4w,rowQ,dma,stream>"
+    assert bench.kernel_label(name)  # demangled names get a label too
