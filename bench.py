@@ -9,8 +9,9 @@ the fp64 oracle timed on the host cores as a CPU baseline.
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--compute bf16|fp32]
                     [--variant plain|cwd|normuon_cwd] [--graph] [--no-peaks]
 
---variant times muon_step_ex instead: page 1's cautious weight decay (cwd,
-decay 0.1) or NorMuon (beta2 0.95, eps 1e-8) with it (normuon_cwd).  The
+--variant times muon_step_ex instead: the cautious weight decay (cwd, decay
+0.1) of the web3.cnoyu.systems review of karpathy/autoresearch's train.py,
+or NorMuon (beta2 0.95, eps 1e-8) with it (normuon_cwd).  The
 default, plain, is the benchmark's Muon step.  --graph times replays of one
 captured step instead of eager calls (the small workloads are bound by the
 host cost of their launches).

@@ -202,7 +202,9 @@ def step(params, grads, bufs, *, mu, lr, scales=None, coeffs=QUINTIC, n_steps=No
 def step_ex(params, grads, bufs, *, mu, lr, scales=None, coeffs=QUINTIC, n_steps=None,
             eps=DEFAULT_EPS, compute="bf16", workspace=None, weight_decay=0.0,
             cautious=True, second_moments=None, beta2=None, normuon_eps=None):
-    """``step`` with page 1's additions (muon_step_ex): decoupled weight decay
+    """``step`` with the additions of the web3.cnoyu.systems review of
+    karpathy/autoresearch's train.py, paragraph after the Muon one
+    (muon_step_ex): decoupled weight decay
     (cautious: only where update * param >= 0) and, when ``second_moments``
     (fp32 vectors of min(rows, cols) elements, in place) are given, NorMuon
     scaling with ``beta2`` and ``normuon_eps`` (no defaults: the page gives

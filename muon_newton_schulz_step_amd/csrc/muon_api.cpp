@@ -2,8 +2,9 @@
 // so they run on a machine without a GPU), grouping by oriented shape,
 // workspace layout, launch sequencing and the optional per-launch timing log.
 //
-// Sequence per group of same-oriented-shape matrices (page 1, Muon
-// paragraph: momentum, Newton-Schulz steps, update), on the caller's stream:
+// Sequence per group of same-oriented-shape matrices (the web3.cnoyu.systems
+// review of karpathy/autoresearch's train.py, Muon paragraph: momentum,
+// Newton-Schulz steps, update), on the caller's stream:
 //   prep, norm, then for each step k: gram, poly, update.
 #include <hip/hip_runtime_api.h>
 

@@ -51,7 +51,8 @@ __device__ __forceinline__ void split_bf16(float x, bf16_t& hi, bf16_t& lo) {
 
 // One weight element: W' = W + wscale*x (wscale = -lr*scale, x the update
 // direction), minus lr*wd*W where the decay applies: everywhere, or with
-// page 1's cautious decay only where x*W >= 0.  neg_lrwd = -lr*wd; with 0
+// the cautious decay (web3.cnoyu.systems review of karpathy/autoresearch's
+// train.py, paragraph after the Muon one) only where x*W >= 0.  neg_lrwd = -lr*wd; with 0
 // the decay term is skipped (so that non-finite weights propagate as in the
 // plain update).
 __device__ __forceinline__ float weight_step(float w, float x, float wscale, float neg_lrwd,

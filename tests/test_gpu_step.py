@@ -197,7 +197,8 @@ def test_stress_full_shape_reduced_batch():
 
 
 def polar_distance_report(o, o_cf, x0, eig, coeffs, i):
-    """Page 1 names the orthogonal factor U of G = U S as the target.  For the
+    """The web3.cnoyu.systems review of karpathy/autoresearch's train.py (Muon
+    paragraph) names the orthogonal factor U of G = U S as the target.  For the
     bf16-rounded G fed here, that factor is P = G (G^T G)^(-1/2) (from the
     Gram eigendecomposition); 30 cubic steps leave directions with tiny
     normalised singular values s unconverged, so O is not P: ||O - P||_F is

@@ -1,5 +1,6 @@
-"""muon_step_ex on the GPU vs the fp64 oracle: page 1's cautious weight
-decay and NorMuon scaling on top of the plain step, mixed shapes (tall,
+"""muon_step_ex on the GPU vs the fp64 oracle: the cautious weight decay and
+NorMuon scaling of the web3.cnoyu.systems review of karpathy/autoresearch's
+train.py (paragraph after the Muon one) on top of the plain step, mixed shapes (tall,
 wide, square, ragged), both compute precisions, and the second-moment
 moving average carried over two steps.
 

@@ -281,7 +281,7 @@ def test_muon_step_update_closed_form():
     assert np.max(np.abs(new_buf - (0.9 * buf + g))) <= 1e-15
 
 
-# ------------------------------------------------- P11 3.8B shape list (page 5)
+# ------- 3.8B shape list ("Training a 3.8B LLM to CORE 0.384 for $998", parameter table)
 def _golden_table():
     path = os.path.join(os.path.dirname(__file__), "golden", "page5_parameter_table.txt")
     out = {}

@@ -1,5 +1,6 @@
-"""Pins of the oracle's NorMuon scaling and cautious weight decay (page 1,
-the paragraph after the Muon one) against facts that do not come from the
+"""Pins of the oracle's NorMuon scaling and cautious weight decay (the
+web3.cnoyu.systems review of karpathy/autoresearch's train.py, the paragraph
+after the Muon one) against facts that do not come from the
 oracle itself: closed forms on orthonormal rows and columns, the RMS
 normalisation that beta2 = 0 implies, the two-step moving average, transpose
 equivariance, a hand-derived decay example and the special cases of the
@@ -130,7 +131,7 @@ def test_step_ex_reduces_to_plain_step():
 
 
 def test_step_ex_order_normuon_then_decay():
-    # page 1: orthogonalise, then NorMuon scaling, then the decayed update
+    # the review's order: orthogonalise, then NorMuon scaling, then the decayed update
     # with the scaled direction; with orthonormal-row NS output the scaling
     # is the closed form of test_normuon_closed_form_on_orthonormal_rows
     m, n = 4, 12
