@@ -36,3 +36,21 @@ def test_degenerate_orthogonalize(kind, shape, compute):
     err = oracle.relative_frobenius_error(to64(o), ref)
     print(kind, shape, compute, "%.3e" % err)
     assert err <= degenerate_tol(kind, compute), (kind, shape, compute, err)
+
+
+def test_empty_calls_launch_nothing():
+    """No matrices: muon_step, muon_step_ex and muon_orthogonalize of a batch
+    of 0 return at once; the per-launch timing log records no launch."""
+    announce("empty calls")
+    mn.timing_enable(True)
+    try:
+        mn.timing_read()
+        mn.step([], [], [], mu=0.95, lr=0.02)
+        mn.step_ex([], [], [], mu=0.95, lr=0.02, weight_decay=0.1)
+        x = torch.empty((0, 256, 384), device=DEV)
+        o = mn.orthogonalize(x, Q5)
+        torch.cuda.synchronize()
+        assert o.shape == (0, 256, 384)
+        assert mn.timing_read() == []
+    finally:
+        mn.timing_enable(False)
