@@ -165,7 +165,11 @@ typedef struct {
   int cautious;        /* 0 or 1 */
   int normuon;         /* 0 or 1: NorMuon scaling with `second_moment` */
   float beta2;         /* NorMuon EMA factor, in [0, 1] */
-  float normuon_eps;   /* NorMuon: finite, >= 0 */
+  float normuon_eps;   /* NorMuon: finite, >= 0.  With 0, a row whose v' is 0
+                          (a zero row of O and a zero v, or beta2 = 1 and a
+                          zero v) divides by zero and its values become
+                          non-finite, as the formula gives; a positive value
+                          avoids that */
 } muon_options;
 
 /* Workspace bytes of muon_step_ex for these shapes and options (NULL
