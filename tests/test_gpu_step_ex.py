@@ -209,3 +209,40 @@ def test_normuon_row_statistics_match_the_applied_update(compute):
         mean_gpu = (v1 - beta2 * v0[k]) / (1.0 - beta2)
         rel = np.abs(mean_gpu - mean_sq) / mean_sq
         assert rel.max() <= 1e-4, (k, (r, c), float(rel.max()), int(rel.argmax()))
+
+
+@pytest.mark.parametrize("compute", ["bf16", "fp32"])
+def test_normuon_zero_eps_zero_row_is_non_finite_like_the_oracle(compute):
+    """normuon_eps = 0 with a zero second moment and a gradient whose row 5
+    (wide) or column 5 (tall) is zero: that line of O stays exactly zero
+    through the iteration, v' is 0 and the scaling divides 0 by 0.  The new
+    weights are non-finite on exactly that line, as in the oracle; the other
+    lines agree with the oracle to the usual bar."""
+    announce("normuon eps 0, zero row", compute)
+    shapes = ((64, 192), (192, 64))
+    w = dataclasses.replace(wl.GPT_D768, shapes=shapes)
+    inp = wl.make_inputs(w, device=DEV)
+    inp["grads"][0][5, :] = 0
+    inp["grads"][1][:, 5] = 0
+    inp["bufs"] = [torch.zeros_like(b) for b in inp["bufs"]]
+    vs = [torch.zeros(min(s), device=DEV) for s in shapes]
+    before = [to64(p) for p in inp["params"]]
+    mn.step_ex(inp["params"], inp["grads"], inp["bufs"], mu=w.mu, lr=w.lr,
+               scales=inp["scales"], coeffs=w.coeff_table, compute=compute,
+               weight_decay=0.0, cautious=False, second_moments=vs, beta2=0.9,
+               normuon_eps=0.0)
+    torch.cuda.synchronize()
+    for k, shape in enumerate(shapes):
+        with np.errstate(invalid="ignore", divide="ignore"):
+            ref = oracle.muon_step_ex(before[k], to64(inp["grads"][k]), np.zeros(shape), w.mu,
+                                      w.lr, inp["scales"][k], w.coeff_table, weight_decay=0.0,
+                                      cautious=False, second_moment=np.zeros(min(shape)),
+                                      beta2=0.9, normuon_eps=0.0)
+        got = to64(inp["params"][k])
+        bad_ref, bad_got = ~np.isfinite(ref["w"]), ~np.isfinite(got)
+        assert bad_ref.any() and np.array_equal(bad_ref, bad_got), (shape, bad_got.sum())
+        line = (slice(5, 6), slice(None)) if k == 0 else (slice(None), slice(5, 6))
+        assert bad_got[line].all() and bad_got.sum() == bad_got[line].size
+        ok = np.isfinite(ref["w"])
+        err = oracle.relative_frobenius_error(got[ok] - before[k][ok], ref["w"][ok] - before[k][ok])
+        assert err <= tol(compute, shape), (shape, err)
