@@ -27,6 +27,12 @@
  *    MUON_ERR_WORKSPACE had no side effect.  MUON_ERR_HIP means a launch
  *    failed; part of the work may already be enqueued.
  *  - Non-finite values in the data propagate; they are not checked.
+ *  - Range: the 1/(||u|| + eps) normalisation is applied inside the first
+ *    Newton-Schulz products, so those accumulate products of the raw
+ *    entries of u (the momentum-corrected gradient) in fp32: entries of
+ *    magnitude between about 1e-18 and 1e16 keep full accuracy (the tests
+ *    cover 2^-60 to 2^55); far larger ones can overflow fp32 in the first
+ *    Gram matrix, far smaller ones lose precision to fp32's normal range.
  *  - Repeated calls on the same inputs give bitwise-identical results (all
  *    reductions use a fixed order; there are no floating-point atomics).
  *  - Calls are re-entrant when they use distinct workspaces.

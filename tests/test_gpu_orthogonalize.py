@@ -148,6 +148,25 @@ def test_scale_invariance():
         assert oracle.relative_frobenius_error(o, np.sign(alpha) * base) <= 1e-4
 
 
+@pytest.mark.parametrize("compute", ["bf16", "fp32"])
+def test_magnitude_range(compute):
+    """The normalisation is folded into the first Gram and update epilogues,
+    so X_0 is stored unnormalised and the first Gram accumulates products of
+    raw entries in fp32.  Entries from 2^-60 (8.7e-19) to 2^55 (3.6e16), K =
+    192: each against the oracle on the same scaled input.  At 2^-60 the norm
+    is far below eps = 1e-7, so X_0 = u / (||u|| + eps) is tiny and the
+    iteration runs in its linear range, in the oracle as on the GPU."""
+    announce("magnitude range", compute)
+    x = wl.gaussian_matrix(64, 192, seed=19, device=DEV)
+    for k in (-60, -30, 30, 55):
+        xs = x * (2.0 ** k)  # exact: a power of two
+        o = to64(mn.orthogonalize(xs, Q5, compute=compute))
+        ref = oracle.orthogonalize(to64(xs), Q5)
+        err = oracle.relative_frobenius_error(o, ref)
+        print(compute, k, "%.3e" % err)
+        assert err <= tol(compute, (64, 192)), (k, err)
+
+
 def test_permutation_invariance():
     announce("permutation invariance")
     x = wl.gaussian_matrix(200, 330, seed=10, device=DEV)
