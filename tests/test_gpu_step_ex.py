@@ -246,3 +246,12 @@ def test_normuon_zero_eps_zero_row_is_non_finite_like_the_oracle(compute):
         ok = np.isfinite(ref["w"])
         err = oracle.relative_frobenius_error(got[ok] - before[k][ok], ref["w"][ok] - before[k][ok])
         assert err <= tol(compute, shape), (shape, err)
+
+
+@pytest.mark.parametrize("compute", ["bf16", "fp32"])
+def test_random_shapes_normuon_cautious(compute):
+    """The seeded sweep of ragged shapes (test_gpu_random_shapes) through
+    muon_step_ex with NorMuon and cautious decay."""
+    from test_gpu_random_shapes import random_shapes
+    run_case(compute, wd=0.1, cautious=True, normuon=True,
+             shapes=random_shapes(200 + (compute == "fp32"), count=10))
