@@ -142,7 +142,9 @@ int muon_orthogonalize(const void* in, int in_dtype, void* out, int out_dtype,
  *   coeffs, n_steps, eps, compute, workspace: as for muon_orthogonalize,
  *                  with the workspace from muon_step_workspace_bytes.
  * params[i], grads[i] and momentum[i] must not overlap one another or the
- * workspace (MUON_ERR_INVALID_ARG).
+ * workspace, and no params or momentum buffer may overlap any other
+ * matrix's buffers (gradients may share memory with each other)
+ * (MUON_ERR_INVALID_ARG).
  * n == 0 returns MUON_OK with nothing enqueued. */
 int muon_step(int n, const int* rows, const int* cols,
               void* const* params, int param_dtype,

@@ -8,6 +8,7 @@
 //   prep, norm, then for each step k: gram, poly, update.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -465,6 +466,25 @@ bool overlap(const void* p, size_t pb, const void* q, size_t qb) {
   return a < b + qb && b < a + pb;
 }
 
+// Byte ranges of a step's buffers.  True when any two written ranges
+// overlap, or a read range overlaps a written one (reads may share memory
+// with each other).  Sorting keeps it O(n log n) for large steps.
+struct Span {
+  uintptr_t lo, hi;
+};
+bool spans_conflict(std::vector<Span>& written, const std::vector<Span>& read) {
+  std::sort(written.begin(), written.end(), [](const Span& a, const Span& b) { return a.lo < b.lo; });
+  for (size_t i = 1; i < written.size(); ++i)
+    if (written[i].lo < written[i - 1].hi) return true;
+  for (const Span& r : read) {
+    // the first written range that ends after r starts
+    auto it = std::upper_bound(written.begin(), written.end(), r.lo,
+                               [](uintptr_t v, const Span& w) { return v < w.hi; });
+    if (it != written.end() && it->lo < r.hi) return true;
+  }
+  return false;
+}
+
 // A step's chunks in launch order: each oriented-shape group split into
 // chunks of at most kChunk matrices.
 struct ChunkRef {
@@ -623,6 +643,27 @@ int step_impl(int n, const int* rows, const int* cols, void* const* params, int 
           overlap(v, vb, momentum[i], el * 4))
         return MUON_ERR_INVALID_ARG;
     }
+  }
+  {
+    // across matrices too: no written buffer may overlap another buffer
+    // that is written, nor a gradient
+    std::vector<Span> written, read;
+    written.reserve(3 * (size_t)n);
+    read.reserve(n);
+    for (int i = 0; i < n; ++i) {
+      const size_t el = (size_t)rows[i] * cols[i];
+      auto span = [](const void* p, size_t b) {
+        const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+        return Span{a, a + b};
+      };
+      written.push_back(span(params[i], el * 4));
+      written.push_back(span(momentum[i], el * 4));
+      if (normuon)
+        written.push_back(span(second_moment[i],
+                               (size_t)(rows[i] < cols[i] ? rows[i] : cols[i]) * 4));
+      read.push_back(span(grads[i], el * gsz));
+    }
+    if (spans_conflict(written, read)) return MUON_ERR_INVALID_ARG;
   }
   if (param_dtype != MUON_FP32) return MUON_ERR_UNSUPPORTED;
   // the allocation-free entry point never forks: its scratch holds one chunk

@@ -120,6 +120,13 @@ def step_call(n=2, rows=(8, 16), cols=(16, 8), params=None, grads=None, bufs=Non
     (dict(ws=FAKE * 64), mn.MUON_ERR_INVALID_ARG),           # workspace overlaps a weight
     (dict(ws=FAKE * 128 + 4096), mn.MUON_ERR_INVALID_ARG),   # ... a gradient
     (dict(ws=FAKE * 64 + 8192 - 256), mn.MUON_ERR_INVALID_ARG),  # ... a momentum buffer
+    # across matrices: two weights in one buffer, a weight over the other
+    # matrix's (bf16) gradient, momentum buffers that overlap by four elements,
+    # a momentum buffer over the other matrix's gradient
+    (dict(params=[FAKE * 64, FAKE * 64]), mn.MUON_ERR_INVALID_ARG),
+    (dict(params=[FAKE * 64, FAKE * 64 + 4096 + 240]), mn.MUON_ERR_INVALID_ARG),
+    (dict(bufs=[FAKE * 64 + 8192, FAKE * 64 + 8192 + 496]), mn.MUON_ERR_INVALID_ARG),
+    (dict(bufs=[FAKE * 64 + 8192, FAKE * 64 + 4096]), mn.MUON_ERR_INVALID_ARG),
 ])
 def test_step_rejects_before_enqueue(kw, expect):
     assert step_call(**kw) == expect
@@ -165,6 +172,11 @@ OPT = dict(weight_decay=0.1, cautious=1, normuon=1, beta2=0.95, normuon_eps=1e-8
     (dict(vs=[FAKE * 64 + 8, FAKE * 128 + 16384]), mn.MUON_ERR_INVALID_ARG),      # overlaps W
     (dict(ws=0), mn.MUON_ERR_WORKSPACE),
     (dict(vs=[FAKE * 4096 + 256, FAKE * 128 + 16384]), mn.MUON_ERR_INVALID_ARG),  # in workspace
+    # the two (8, 16) and (16, 8) matrices keep 8 floats of second moment
+    # each: sharing one buffer, or overlapping the other matrix's weight
+    (dict(vs=[FAKE * 64 + 16384, FAKE * 64 + 16384]), mn.MUON_ERR_INVALID_ARG),
+    (dict(vs=[FAKE * 64 + 16384, FAKE * 64 + 16384 + 28]), mn.MUON_ERR_INVALID_ARG),
+    (dict(vs=[FAKE * 64 + 16384, FAKE * 64 + 508]), mn.MUON_ERR_INVALID_ARG),
 ])
 def test_step_ex_rejects_before_enqueue(kw, expect):
     assert step_ex_call(**kw) == expect
@@ -274,6 +286,7 @@ def static_call(n=2, rows=(8, 16), cols=(16, 8), params=None, grads=None, bufs=N
     (dict(rows=(8, 0)), mn.MUON_ERR_INVALID_ARG),
     (dict(params=[FAKE * 64, 0]), mn.MUON_ERR_INVALID_ARG),
     (dict(bufs=[FAKE * 64, FAKE * 128 + 8192]), mn.MUON_ERR_INVALID_ARG),
+    (dict(params=[FAKE * 64, FAKE * 64]), mn.MUON_ERR_INVALID_ARG),
     (dict(param_dtype=0), mn.MUON_ERR_UNSUPPORTED),
     (dict(mu=float("nan")), mn.MUON_ERR_INVALID_ARG),
     (dict(n_steps=65, coeffs=Q * 13), mn.MUON_ERR_INVALID_ARG),

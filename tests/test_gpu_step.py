@@ -276,3 +276,29 @@ def test_non_finite_values_propagate_like_the_oracle():
     assert torch.equal(dirty["params"][1][keep], clean["params"][1][keep])
     assert torch.equal(dirty["params"][2], clean["params"][2])
     assert torch.equal(dirty["bufs"][2], clean["bufs"][2])
+
+
+def test_shared_gradient_and_aliasing_refused():
+    """Gradients are only read, so two matrices may take the same gradient
+    tensor: the result is bitwise that of two separate copies.  A weight
+    tensor passed for two matrices is refused before anything runs."""
+    announce("shared gradient")
+    w = dataclasses.replace(wl.GPT_D768, shapes=((300, 700), (300, 700), (700, 300)))
+    a = wl.make_inputs(w, device=DEV)
+    b = {k: ([t.clone() for t in v] if k in ("params", "bufs") else v) for k, v in a.items()}
+    shared = [a["grads"][0], a["grads"][0], a["grads"][2]]
+    copies = [a["grads"][0].clone(), a["grads"][0].clone(), a["grads"][2]]
+    for inp, grads in ((a, shared), (b, copies)):
+        mn.step(inp["params"], grads, inp["bufs"], mu=w.mu, lr=w.lr, scales=inp["scales"],
+                coeffs=w.coeff_table, compute="bf16")
+    torch.cuda.synchronize()
+    for x, y in zip(a["params"] + a["bufs"], b["params"] + b["bufs"]):
+        assert torch.equal(x, y)
+    kept = [p.clone() for p in a["params"]]
+    with pytest.raises(mn.MuonError) as err:
+        mn.step([a["params"][0], a["params"][0]], shared[:2], a["bufs"][:2], mu=w.mu,
+                lr=w.lr, compute="bf16")
+    assert err.value.status == mn.MUON_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    for x, y in zip(a["params"], kept):
+        assert torch.equal(x, y)
