@@ -79,6 +79,13 @@ def parse():
                    help="print a markdown table of a rocprofv3 --kernel-trace CSV: the "
                         "library's kernels by instantiation and grid, calls, average and "
                         "total time")
+    p.add_argument("--tile-sweep", action="store_true",
+                   help="time one step over each of a list of same-shape sets (one chunk "
+                        "each, alone) and print per-kernel launch times, one JSON line per "
+                        "set; run with MUON_GEMM_TILE=128, =256 and unset to compare the "
+                        "tiles with the library's choice")
+    p.add_argument("--tile-table", nargs=3, metavar=("AT128", "AT256", "CHOSEN"),
+                   help="markdown table of three --tile-sweep outputs")
     p.add_argument("--write-mfma", metavar="MFMA_CSV",
                    help="turn a rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 "
                         "SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE counter CSV of a "
@@ -148,13 +155,34 @@ def traffic_from_profiles(kernel_key):
         return None
 
 
+def pick_tile(t256, batch, use, compute="bf16"):
+    """The GEMM tile the library takes for a launch of `batch` matrices with
+    t256 tiles each at 256 x 256, as its host runtime decides it.  use:
+    "full" (update, final), "tri" (polynomial, Q A Q products: the lower
+    triangle of t256 x t256 tiles) or "gram" (the Gram's lower triangle).
+    Rounds of the 256 CUs, one 256-tile workgroup or two 128-tile ones per
+    CU; 256 when 1.6 (the Gram: 1.4) x rounds(256) <= rounds(128).
+    MUON_GEMM_TILE=128|256 forces the tile, as in the library."""
+    if compute != "bf16":
+        return 128
+    pref = os.environ.get("MUON_GEMM_TILE", "")
+    if pref in ("128", "256"):
+        return int(pref)
+    tri = use != "full"
+    t = t256 * (t256 + 1) // 2 if tri else t256
+    t128 = (2 * t256) * (2 * t256 + 1) // 2 if tri else 4 * t256
+    w256, w128 = t * batch, t128 * batch
+    ratio5 = 7 if use == "gram" else 8
+    return 256 if ratio5 * -(-w256 // 256) <= 5 * -(-w128 // 512) else 128
+
+
 def launch_sequence(w):
     """(kind, m, n) of every library launch of one bf16 step, in launch order:
     per oriented group (first appearance) and chunk of at most 64 matrices,
     prep, norm, then gram, poly, update per Newton-Schulz step, the last
     update being one final launch for the chunk's wide matrices and one for
-    its tall ones (a single one for both when neither part alone fills 512
-    tiles of 256 x 256).  Groups with padded N >= 4M and M >= 2048 form the Gram
+    its tall ones (a single one for both when the larger part alone would take
+    128 x 128 tiles).  Groups with padded N >= 4M and M >= 2048 form the Gram
     matrix of steps 1 and 3 (not the last) in two gramq launches instead."""
     def pad(d):
         return (d + 255) // 256 * 256
@@ -168,8 +196,9 @@ def launch_sequence(w):
             chunk = talls[b0:b0 + 64]
             nt = sum(chunk)
             nw = len(chunk) - nt
-            # one launch for both parts when neither fills 512 tiles of 256 x 256
-            mixed = nw > 0 and nt > 0 and max(nw, nt) * (pad(m) // 256) * (pad(n) // 256) < 512
+            # one launch for both parts when the larger would take 128-tiles
+            t256 = (pad(m) // 256) * (pad(n) // 256)
+            mixed = nw > 0 and nt > 0 and pick_tile(t256, max(nw, nt), "full") == 128
             finals = [("final", m, n)] * (1 if mixed else (nw > 0) + (nt > 0))
             seq += [("prep", m, n), ("norm", m, n)]
             for k in range(w.n_steps):
@@ -199,15 +228,17 @@ def ns_flops_executed(w, compute="bf16"):
         for b0 in range(0, count, 64):
             cnt = min(64, count - b0)
             t256 = M // 256
-            tile = 256 if compute == "bf16" and t256 * (t256 + 1) // 2 * cnt >= 512 else 128
-            tri = (M // tile) * (M // tile + 1) // 2 * tile * tile * cnt  # C elements computed
+            def tri(tile):  # C elements the triangle launches compute
+                return (M // tile) * (M // tile + 1) // 2 * tile * tile * cnt
+            tri_g = tri(pick_tile(t256, cnt, "gram", compute))
+            tri_p = tri(pick_tile(t256, cnt, "tri", compute))
             qaq = compute == "bf16" and N >= 4 * M and M >= 2048
             for k in range(w.n_steps):
                 if qaq and k in (1, 3) and k <= w.n_steps - 2:
-                    tot += 2 * (2.0 * tri * M)
+                    tot += 2 * (2.0 * tri_p * M)       # two Q A Q products
                 else:
-                    tot += 2.0 * tri * N
-                tot += 2.0 * tri * M                   # POLY
+                    tot += 2.0 * tri_g * N             # GRAM
+                tot += 2.0 * tri_p * M                 # POLY
                 tot += 2.0 * M * N * M * cnt           # UPDATE / FINAL (full tiles)
     return tot
 
@@ -536,11 +567,93 @@ def measure_vendor_gemm(torch, dev, w):
     return out
 
 
+# Same-shape sets of --tile-sweep: (count, rows, cols), square and wide, from
+# under one round of 256 x 256 tiles on the 256 CUs to about eight.
+TILE_SWEEP_SETS = ([(c, 1280, 1280) for c in (8, 12, 16, 20, 24)]
+                   + [(c, 1024, 1024) for c in (16, 24, 32)]
+                   + [(c, 768, 768) for c in (32, 48, 64)]
+                   + [(c, 1536, 1536) for c in (8, 10, 14)]
+                   + [(c, 2048, 2048) for c in (4, 6, 8)]
+                   + [(8, 1280, 5120), (20, 1280, 5120), (16, 768, 3072), (8, 1024, 4096),
+                      (4, 2048, 8192)])
+
+
+def tile_sweep(torch, mn, wl, reps=11):
+    """One JSON line per set: the median step time over `reps` eager steps and
+    the median launch time of each kernel kind (HIP events of the library)."""
+    import dataclasses
+    dev = "cuda:0"
+    for cnt, r, c in TILE_SWEEP_SETS:
+        w = dataclasses.replace(wl.GPT_D768, name=f"{cnt}x{r}x{c}", shapes=((r, c),) * cnt)
+        inp = wl.make_inputs(w, device=dev)
+        ws = torch.empty(mn.step_workspace_bytes(w.shapes, "bf16"), dtype=torch.uint8,
+                         device=dev)
+
+        def run():
+            mn.step(inp["params"], inp["grads"], inp["bufs"], mu=w.mu, lr=w.lr,
+                    scales=inp["scales"], coeffs=w.coeff_table, workspace=ws)
+        for _ in range(3):
+            run()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            run()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        mn.timing_enable(True)
+        mn.timing_read()
+        for _ in range(5):
+            run()
+        torch.cuda.synchronize()
+        mn.timing_enable(False)
+        per = {}
+        for rec in mn.timing_read():
+            per.setdefault(rec["kind"], []).append(rec["ms"])
+        t256, n256 = -(-r // 256), -(-c // 256)
+        print(json.dumps({
+            "set": w.name, "count": cnt, "rows": r, "cols": c,
+            "tile_env": os.environ.get("MUON_GEMM_TILE", ""),
+            "tiles": {"gram": pick_tile(t256, cnt, "gram"), "poly": pick_tile(t256, cnt, "tri"),
+                      "update": pick_tile(t256 * n256, cnt, "full")},
+            "step_ms": round(sorted(ts)[len(ts) // 2], 4),
+            "kinds": {k: round(sorted(v)[len(v) // 2], 4) for k, v in per.items()}}), flush=True)
+        del inp, ws
+        torch.cuda.empty_cache()
+
+
+def tile_table(paths):
+    """Markdown: per set, step and per-kernel times at 128 and 256 tiles and
+    with the library's choice (the outputs of three --tile-sweep runs)."""
+    runs = []
+    for p in paths:
+        runs.append({d["set"]: d for d in (json.loads(l) for l in open(p) if l.startswith("{"))})
+    print("| set | tiles at 256 (triangle / full) | step ms 128 / 256 / chosen | chosen tiles "
+          "(gram / poly / full) | gram | poly | update | final |")
+    print("|---|---|---|---|---|---|---|---|")
+    for name, ch in runs[2].items():
+        a, b = runs[0][name], runs[1][name]
+        t, n = -(-ch["rows"] // 256), -(-ch["cols"] // 256)
+        cells = []
+        for k in ("gram", "poly", "update", "final"):
+            pick = ch["tiles"][k if k in ("gram", "poly") else "update"]
+            x, y = a["kinds"][k], b["kinds"][k]
+            best = "128" if x < y else "256"
+            cells.append(f"{x:.3f} / {y:.3f}" + (" ✓" if str(pick) == best else ""))
+        print(f"| {name} | {t * (t + 1) // 2 * ch['count']} / {t * n * ch['count']} | "
+              f"{a['step_ms']:.3f} / {b['step_ms']:.3f} / {ch['step_ms']:.3f} | "
+              f"{ch['tiles']['gram']} / {ch['tiles']['poly']} / {ch['tiles']['update']} | "
+              + " | ".join(cells) + " |")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the Muon step shards by whole matrix and "
-              f"this build runs one GPU's share; --gpus {args.gpus} is not supported.",
+              f"this library runs one GPU's share; --gpus {args.gpus} is not supported.",
               file=sys.stderr)
         sys.exit(2)
     import torch
@@ -549,6 +662,12 @@ def main():
 
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
+        return
+    if args.tile_table:
+        tile_table(args.tile_table)
+        return
+    if args.tile_sweep:
+        tile_sweep(torch, mn, wl)
         return
     w = wl.WORKLOADS[args.workload]
     full_count = len(w.shapes)

@@ -62,11 +62,31 @@ int stream_pref() {
   return v;
 }
 
-// 256 x 256 tiles unless that leaves fewer than two blocks per CU.
-int pick_tile(bool cbf16, long long tiles_at_256, int batch) {
+// What a GEMM launch computes, for its choice of tile: every tile of the
+// output (update, final), the lower triangle (polynomial, the Q A Q
+// products), or the lower triangle of the Gram matrix.
+enum class TileUse { full, tri, gram };
+
+// Tile of a bf16 GEMM launch of `batch` matrices with t256 tiles each at
+// 256 x 256 (tri, gram: the lower triangle of t256 x t256 tiles, so at
+// 128 x 128 the triangle of 2 t256 x 2 t256; full: four times as many).
+// A launch runs in rounds over the 256 CUs: a 256-tile workgroup fills a
+// CU, two 128-tile workgroups share one.  A round of 128-tile workgroups
+// takes about 1/1.6 of a round of 256-tile ones (four times fewer flops
+// each, half the operand reuse; 1/1.4 for the Gram, whose epilogue is the
+// lightest), so the larger tile wins when 1.6 (1.4) x rounds(256) <=
+// rounds(128).  The ratios are fitted to single-chunk steps of 4 to 64
+// matrices from 768 x 768 to 2048 x 8192 timed at both tiles.
+int pick_tile(bool cbf16, long long t256, int batch, TileUse use) {
   const int pref = tile_pref();
   if (pref == 128 || pref == 256) return gemm_tile(cbf16, pref);
-  return gemm_tile(cbf16, tiles_at_256 * batch >= 512 ? 256 : 128);
+  const bool tri = use != TileUse::full;
+  const long long t = tri ? t256 * (t256 + 1) / 2 : t256;
+  const long long t128 = tri ? (2 * t256) * (2 * t256 + 1) / 2 : 4 * t256;
+  const long long w256 = t * batch, w128 = t128 * batch;
+  const long long r256 = (w256 + 255) / 256, r128 = (w128 + 511) / 512;
+  const long long ratio5 = use == TileUse::gram ? 7 : 8;  // 5 x the ratio
+  return gemm_tile(cbf16, ratio5 * r256 <= 5 * r128 ? 256 : 128);
 }
 
 // Workspace regions for `cnt` matrices of oriented shape m x n (padded
@@ -267,13 +287,17 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
   if (err != hipSuccess) return MUON_ERR_HIP;
 
   const int t256 = L.M / 256;
-  const int tile_sym = pick_tile(cbf16, (long long)t256 * (t256 + 1) / 2, c.cnt);
-  const int tile_upd = pick_tile(cbf16, (long long)t256 * (L.N / 256), c.cnt);
+  const int tile_gram = pick_tile(cbf16, t256, c.cnt, TileUse::gram);
+  const int tile_sym = pick_tile(cbf16, t256, c.cnt, TileUse::tri);
+  const int tile_upd = pick_tile(cbf16, (long long)t256 * (L.N / 256), c.cnt, TileUse::full);
   // flops the MFMAs execute: lower-triangle tiles of M x M for the Gram and
   // polynomial launches (K = N or M), all M x N for the update
-  const double tsym = L.M / tile_sym;
-  const double tri_el = tsym * (tsym + 1) / 2 * (double)tile_sym * tile_sym;
-  const double x_gram = 2.0 * tri_el * L.N * cnt, x_sym = 2.0 * tri_el * L.M * cnt;
+  auto tri_el = [&](int tile) {
+    const double t = L.M / tile;
+    return t * (t + 1) / 2 * (double)tile * tile;
+  };
+  const double x_gram = 2.0 * tri_el(tile_gram) * L.N * cnt,
+               x_sym = 2.0 * tri_el(tile_sym) * L.M * cnt;
   const double x_upd = 2.0 * (double)L.M * L.N * L.M;  // per matrix
   for (int k = 0; k < n_steps; ++k) {
     const bool first = k == 0, last = k == n_steps - 1;
@@ -314,14 +338,16 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
       g.sP = g.sQ = MN; g.ldp = g.ldq = L.N; g.K = L.N;
       g.C = A; g.sC = MM; g.ldc = L.M;
       g.Clo = L.qaq && qaq_step(k + 1, n_steps) ? Alo : nullptr;
+      g.tiles_m = g.tiles_n = L.M / tile_gram;
       err = timed(MUON_K_GRAM, L.m, L.n, c.cnt, k, cnt * 2.0 * m * m * n, x_gram,
                   pmn * es + pmm * es * (g.Clo ? 1.5 : 1.0), s,
                   [&] {
-                    return launch_gemm(cbf16, g.Clo ? EPI_GRAM_LO : EPI_GRAM, tile_sym, g, c.wt,
+                    return launch_gemm(cbf16, g.Clo ? EPI_GRAM_LO : EPI_GRAM, tile_gram, g, c.wt,
                                        c.cnt, s);
                   });
       if (err != hipSuccess) return MUON_ERR_HIP;
       g.Clo = nullptr;
+      g.tiles_m = g.tiles_n = L.M / tile_sym;
     }
 
     // B = b A + c A A (K = M)
@@ -392,13 +418,14 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
       const int nwide = c.cnt - ntall;
       const long long t256_mat = (long long)t256 * (L.N / 256);
       const bool mix = cbf16 && c.final_mode == FINAL_WEIGHTS && nwide > 0 && ntall > 0 &&
-                       pick_tile(cbf16, t256_mat, nwide > ntall ? nwide : ntall) == 128;
+                       pick_tile(cbf16, t256_mat, nwide > ntall ? nwide : ntall,
+                                 TileUse::full) == 128;
       for (int part = 0; part < (mix ? 1 : 2) && err == hipSuccess; ++part) {
         const int b = mix ? c.cnt : part == 0 ? nwide : ntall;
         if (b == 0) continue;
         GemmArgs gf = g;
         gf.mat0 = part == 0 ? 0 : nwide;
-        const int tile_f = mix ? 128 : pick_tile(cbf16, t256_mat, b);
+        const int tile_f = mix ? 128 : pick_tile(cbf16, t256_mat, b, TileUse::full);
         gf.tiles_m = L.M / tile_f; gf.tiles_n = L.N / tile_f;
         const int epi = mix ? EPI_FINAL_W_MIX
                         : c.final_mode == FINAL_WEIGHTS ? (part ? EPI_FINAL_W_T : EPI_FINAL_W)

@@ -45,9 +45,29 @@ def test_launch_sequence_mixed_final_when_parts_are_small():
     assert finals == [(768, 768), (768, 3072)]
 
 
+def test_tile_choice_model():
+    # rounds of the 256 CUs: 256-tiles when 1.6 rounds of 128-tiles (1.4 for
+    # the Gram) per round of 256 make up for the larger tile
+    pt = bench.pick_tile
+    assert pt(12 * 48, 56, "full") == 256   # 3.8B update: 126 vs 252 rounds
+    assert pt(12, 56, "gram") == 256        # its Gram: 18 vs 33
+    assert pt(12, 56, "tri") == 256         # and polynomial
+    assert pt(4, 56, "tri") == 128          # (1024, 3072) polynomial: 3 vs 4
+    assert pt(4, 56, "gram") == 128         # its Gram: 1.4 x 3 > 4
+    assert pt(4 * 12, 56, "full") == 256    # its update: 3 vs 6
+    assert pt(25, 16, "full") == 256        # 16 x 1280^2 update: 2 vs 4
+    assert pt(25, 12, "full") == 128        # 12 x 1280^2: 2 vs 3
+    assert pt(25, 8, "full") == 256         # 8 x 1280^2: 1 vs 2
+    assert pt(5, 20, "gram") == 256         # 20 x 1280^2 Gram: 1.4 x 2 <= 3
+    assert pt(5, 20, "tri") == 128          # its polynomial: 1.6 x 2 > 3
+    assert pt(5, 8, "tri") == 128           # 8 x 1280^2: 1 vs 1
+    assert pt(8, 4, "gram") == 256          # 4 x 2048 x 8192 Gram: 1 vs 2
+    assert pt(12 * 48, 56, "full", "fp32") == 128
+
+
 def test_executed_flops_of_the_3p8b_step():
     # the figure the MFMA counters measured on the GPU (profiles/mfma.json)
-    assert bench.ns_flops_executed(wl.GPT_3P8B) == 139004469051392.0
+    assert bench.ns_flops_executed(wl.GPT_3P8B) == 138854145196032.0
     # counted: the method's 4 m^2 n + 2 m^3 per matrix and step
     assert abs(wl.GPT_3P8B.ns_flops_counted() - 1.99029e14) < 1e9
 
