@@ -31,7 +31,7 @@ def test_launch_sequence_of_the_3p8b_step():
         assert g.count("update") == 4 and g.count("final") == 1 and len(g) == 17
     # the 3072 x 12288 group: the Gram matrix of steps 1 and 3 formed as
     # Q A Q (two launches counted as gramq each), one final per orientation
-    # (28 + 28, each part alone fills 512 tiles of 256 x 256)
+    # (28 + 28, each part alone takes 256 x 256 tiles: 63 rounds of the CUs)
     g = groups[(3072, 12288)]
     assert g.count("gram") == 3 and g.count("gramq") == 4 and g.count("poly") == 5
     assert g.count("update") == 4 and g.count("final") == 2
