@@ -1,6 +1,7 @@
 """Host-side logic of bench.py, on the CPU: the refusal of several GPUs,
 the launch-sequence model the counter summaries are matched against, the
 executed-flop count, and the labels given to kernel names."""
+import json
 import os
 import subprocess
 import sys
@@ -79,3 +80,30 @@ def test_kernel_labels():
     mixed = "_ZN4muon11gemm_kernelIDF16bLi10ELi128ELi128ELi2ELi2ELi2ELb1ELb0ELb1EEEvNS_10GemmLaunchE"
     assert bench.kernel_label(mixed) == "gemm<bf16,FINAL_W_MIX,128x128,4w,rowQ,dma,stream>"
     assert bench.kernel_label(name)  # demangled names get a label too
+
+
+def test_tile_table_marks_the_faster_tile(tmp_path, capsys):
+    # three --tile-sweep outputs of one set: the table shows both tiles'
+    # launch times and marks the kinds where the chosen tile is the faster
+    def line(env, step, kinds, tiles):
+        return json.dumps({"set": "4x2048x2048", "count": 4, "rows": 2048, "cols": 2048,
+                           "tile_env": env, "tiles": tiles, "step_ms": step, "kinds": kinds})
+    chosen = {"gram": 256, "poly": 256, "update": 128}
+    paths = []
+    for env, step, kinds in (
+            ("128", 1.05, {"gram": 0.054, "poly": 0.057, "update": 0.076, "final": 0.101}),
+            ("256", 0.97, {"gram": 0.049, "poly": 0.051, "update": 0.075, "final": 0.093}),
+            ("", 0.99, {"gram": 0.049, "poly": 0.051, "update": 0.076, "final": 0.101})):
+        p = tmp_path / f"ts_{env or 'auto'}.jsonl"
+        p.write_text(line(env, step, kinds, chosen) + "\n")
+        paths.append(str(p))
+    bench.tile_table(paths)
+    rows = [r for r in capsys.readouterr().out.splitlines() if r.startswith("| 4x2048")]
+    assert len(rows) == 1
+    cells = [c.strip() for c in rows[0].strip("|").split("|")]
+    assert cells[1] == "144 / 256"   # tiles at 256 over the 4 matrices: triangle / full
+    assert cells[2] == "1.050 / 0.970 / 0.990"
+    assert cells[3] == "256 / 256 / 128"
+    assert cells[4].endswith("✓") and cells[5].endswith("✓")   # 256 was faster
+    assert not cells[6].endswith("✓")                  # update: 256 faster, 128 chosen
+    assert not cells[7].endswith("✓")
