@@ -86,6 +86,9 @@ def parse():
                         "tiles with the library's choice")
     p.add_argument("--tile-table", nargs=3, metavar=("AT128", "AT256", "CHOSEN"),
                    help="markdown table of three --tile-sweep outputs")
+    p.add_argument("--overlap-probe", action="store_true",
+                   help="run the library's MFMA probe and copy probe alone and side by side "
+                        "on two streams (one long launch each) and print what each sustains")
     p.add_argument("--write-mfma", metavar="MFMA_CSV",
                    help="turn a rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 "
                         "SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE counter CSV of a "
@@ -625,6 +628,57 @@ def tile_sweep(torch, mn, wl, reps=11):
         torch.cuda.empty_cache()
 
 
+def overlap_probe(torch, mn, copy_gib=32, reps=2):
+    """The two probes alone, then the copy launched first and the MFMA probe
+    right after it on a second stream, so both run on the same CUs: one JSON
+    line with each one's rate alone, and while both run.  The copy's rate
+    while the MFMA probe runs is estimated from its total time, taking the
+    rest of the copy at its solo rate."""
+    dev = "cuda:0"
+    s_m, s_c = torch.cuda.Stream(dev), torch.cuda.Stream(dev)
+    sink = torch.empty(1024 * 512, dtype=torch.float32, device=dev)
+    src = torch.empty(copy_gib << 30, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+
+    def launch(stream, fn):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            a.record(stream)
+            work = fn()
+            b.record(stream)
+        return a, b, work
+    mfma = lambda blocks, iters: launch(s_m, lambda: mn.probe_mfma_bf16(sink, blocks, iters))
+    copy = lambda blocks: launch(s_c, lambda: mn.probe_copy(src, dst, blocks))
+    mfma(256, 1000)
+    copy(256)
+    torch.cuda.synchronize()
+    out = {}
+    a, b, fl = mfma(256, 90000)
+    torch.cuda.synchronize()
+    out["mfma_alone"] = {"tflops": round(fl / (a.elapsed_time(b) * 1e-3) / 1e12, 1),
+                         "ms": round(a.elapsed_time(b), 2)}
+    a, b, mv = copy(256)
+    torch.cuda.synchronize()
+    solo = a.elapsed_time(b)
+    out["copy_alone"] = {"gbs": round(mv / (solo * 1e-3) / 1e9, 1), "ms": round(solo, 2)}
+    out["both"] = []
+    for _ in range(reps):
+        ca, cb, mv = copy(256)
+        ma, mb, fl = mfma(256, 90000)
+        torch.cuda.synchronize()
+        tm, tc = ma.elapsed_time(mb), ca.elapsed_time(cb)
+        rest = max(0.0, tc - tm)
+        during = max(0.0, mv - mv * rest / solo) / (tm * 1e-3) / 1e9
+        out["both"].append({"mfma_tflops": round(fl / (tm * 1e-3) / 1e12, 1),
+                            "mfma_ms": round(tm, 2), "copy_ms": round(tc, 2),
+                            "copy_gbs_while_mfma_runs": round(during, 1)})
+    out["how"] = (f"256 workgroups of 8 MFMA waves (2 per SIMD, 4 independent chains each, "
+                  f"90000 rounds); a {copy_gib} GiB copy, 256 workgroups of 256 threads, "
+                  f"16-byte accesses; HIP events on each stream")
+    print(json.dumps(out), flush=True)
+
+
 def tile_table(paths):
     """Markdown: per set, step and per-kernel times at 128 and 256 tiles and
     with the library's choice (the outputs of three --tile-sweep runs)."""
@@ -668,6 +722,9 @@ def main():
         return
     if args.tile_sweep:
         tile_sweep(torch, mn, wl)
+        return
+    if args.overlap_probe:
+        overlap_probe(torch, mn)
         return
     w = wl.WORKLOADS[args.workload]
     full_count = len(w.shapes)
