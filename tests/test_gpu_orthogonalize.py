@@ -70,6 +70,19 @@ def test_in_place():
         assert oracle.relative_frobenius_error(to64(x[b]), ref[b]) <= 1e-4
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("compute", ["bf16", "fp32"])
+def test_in_place_across_chunks(compute, dtype):
+    # 70 tall matrices run as two chunks (64 + 6); writing each chunk's
+    # output over its own input gives bitwise the out-of-place result
+    announce("in place across chunks", compute, dtype)
+    x = wl.gaussian_batch(70, 96, 40, seed=8, device=DEV).to(dtype)
+    o = mn.orthogonalize(x, Q5, compute=compute, out_dtype=dtype)
+    mn.orthogonalize(x, Q5, compute=compute, out=x)
+    torch.cuda.synchronize()
+    assert torch.equal(x, o)
+
+
 @pytest.mark.parametrize("compute", ["bf16", "fp32"])
 def test_transpose_equivalence_is_bitwise(compute):
     # a tall matrix runs the same oriented kernels on the same data as its
