@@ -449,10 +449,13 @@ def host_info():
     return blas, threads, model
 
 
-def cpu_baseline(w, seconds, variant="plain"):
+def cpu_baseline(w, seconds, variant="plain", dev="cpu", keep=None):
     """The fp64 oracle on a bounded sample of the workload: matrices taken
     round-robin over the oriented groups until about `seconds` of CPU work,
-    per-group mean times extrapolated by the group counts."""
+    per-group mean times extrapolated by the group counts.  The inputs are
+    made on `dev` and copied to the host; with `keep` (a list), each sampled
+    matrix's (index, inputs on dev, second moment or None, oracle weights)
+    is appended to it."""
     import oracle
     import workloads as wl
     blas, threads, model = host_info()
@@ -467,22 +470,26 @@ def cpu_baseline(w, seconds, variant="plain"):
             if rnd >= len(members[key]):
                 continue
             idx = members[key][rnd]
-            x = wl.make_inputs(w, device="cpu", indices=[idx])
-            g = x["grads"][0].double().numpy()
-            b = x["bufs"][0].double().numpy()
-            p = x["params"][0].double().numpy()
+            x = wl.make_inputs(w, device=dev, indices=[idx])
+            g = x["grads"][0].double().cpu().numpy()
+            b = x["bufs"][0].double().cpu().numpy()
+            p = x["params"][0].double().cpu().numpy()
             opt = VARIANTS[variant]
+            vt = (wl.make_second_moment(w, idx, device=dev)
+                  if opt is not None and "beta2" in opt else None)
             t0 = time.perf_counter()
             if opt is None:
-                oracle.muon_step(p, g, b, w.mu, w.lr, x["scales"][0], w.coeff_table)
+                new_w = oracle.muon_step(p, g, b, w.mu, w.lr, x["scales"][0], w.coeff_table)[0]
             else:
-                v = (wl.make_second_moment(w, idx).double().numpy()
-                     if "beta2" in opt else None)
-                oracle.muon_step_ex(p, g, b, w.mu, w.lr, x["scales"][0], w.coeff_table,
-                                    weight_decay=opt["weight_decay"], cautious=opt["cautious"],
-                                    second_moment=v, beta2=opt.get("beta2", 0.0),
-                                    normuon_eps=opt.get("normuon_eps", 0.0))
+                v = vt.double().cpu().numpy() if vt is not None else None
+                new_w = oracle.muon_step_ex(p, g, b, w.mu, w.lr, x["scales"][0], w.coeff_table,
+                                            weight_decay=opt["weight_decay"],
+                                            cautious=opt["cautious"], second_moment=v,
+                                            beta2=opt.get("beta2", 0.0),
+                                            normuon_eps=opt.get("normuon_eps", 0.0))["w"]
             dt = time.perf_counter() - t0
+            if keep is not None:
+                keep.append((idx, x, vt, p, new_w))
             times[key].append(dt)
             spent += dt
         rnd += 1
@@ -501,6 +508,40 @@ def cpu_baseline(w, seconds, variant="plain"):
         "blas": blas,
         "cpu_model": model,
     }
+
+
+def sample_parity(torch, mn, w, kept, variant, compute):
+    """The library's step on the CPU baseline's sampled matrices (their own
+    step, from the seeded state, the same tensors the oracle was given)
+    against the oracle's weights: relative Frobenius error of dW = W' - W per
+    matrix."""
+    import oracle
+    if not kept:
+        return None
+    params = [x["params"][0].clone() for _, x, _, _, _ in kept]
+    grads = [x["grads"][0] for _, x, _, _, _ in kept]
+    bufs = [x["bufs"][0].clone() for _, x, _, _, _ in kept]
+    scales = [x["scales"][0] for _, x, _, _, _ in kept]
+    opt = VARIANTS[variant]
+    kw = dict(mu=w.mu, lr=w.lr, scales=scales, coeffs=w.coeff_table, compute=compute)
+    if opt is None:
+        mn.step(params, grads, bufs, **kw)
+    else:
+        vs = [vt.clone() for _, _, vt, _, _ in kept] if "beta2" in opt else None
+        mn.step_ex(params, grads, bufs, **kw, weight_decay=opt["weight_decay"],
+                   cautious=opt["cautious"], second_moments=vs, beta2=opt.get("beta2"),
+                   normuon_eps=opt.get("normuon_eps"))
+    torch.cuda.synchronize()
+    errs = []
+    for (idx, _, _, p, new_w), q in zip(kept, params):
+        dw = q.double().cpu().numpy() - p
+        errs.append(oracle.relative_frobenius_error(dw, new_w - p))
+    return {"matrices": len(errs), "max_rel_err_dW": float(f"{max(errs):.3e}"),
+            "mean_rel_err_dW": float(f"{sum(errs) / len(errs):.3e}"),
+            "bar": 2e-2 if compute == "bf16" else 1e-4,
+            "how": "the CPU baseline's sampled matrices as one step of their own from the "
+                   "seeded state, dW = W' - W against the fp64 oracle's, relative Frobenius "
+                   "error per matrix"}
 
 
 def measure_peaks(torch, mn, dev):
@@ -871,9 +912,12 @@ def main():
         elementwise["prep_frac_of_measured_copy"] = round(
             prep_moved / (prep_ms * 1e-3) / 1e9 / peaks["copy_gbs"], 4)
 
-    cpu = None
+    cpu = parity = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, args.cpu_sample_seconds, args.variant)
+        kept = []
+        cpu = cpu_baseline(w, args.cpu_sample_seconds, args.variant, dev=dev, keep=kept)
+        parity = sample_parity(torch, mn, w, kept, args.variant, args.compute)
+        del kept
 
     groups = w.oriented_groups()
     out = {
@@ -912,6 +956,7 @@ def main():
         "elementwise": elementwise,
         "roofline": roof,
         "cpu_baseline": cpu,
+        "parity": parity,
         "kernels": [{k2: (round(v, 4) if isinstance(v, float) else v) for k2, v in k.items()
                      if k2 in ("kind", "m", "n", "batch", "launches", "ms_per_step",
                                "avg_launch_ms", "tflops", "tflops_counted", "gbs")}
