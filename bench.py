@@ -142,20 +142,25 @@ def kernel_source_digest():
     return h.hexdigest()
 
 
-def traffic_from_profiles(kernel_key):
-    """HBM bytes per launch of a kernel from the committed counter summary,
-    or None if there is none for the current kernel source."""
-    if not os.path.exists(TRAFFIC_JSON):
+def profile_entry(path, kernel_key):
+    """A kernel's entry of a committed counter summary (profiles/*.json), or
+    None if there is none for the current kernel source."""
+    if not os.path.exists(path):
         return None
     try:
-        with open(TRAFFIC_JSON) as f:
+        with open(path) as f:
             data = json.load(f)
         if data.get("kernel_source_sha256") != kernel_source_digest():
             return None
-        k = data["kernels"].get(kernel_key)
-        return None if k is None else k["traffic_bytes"]
+        return data["kernels"].get(kernel_key)
     except Exception:
         return None
+
+
+def traffic_from_profiles(kernel_key):
+    """HBM bytes per launch of a kernel from the committed counter summary."""
+    k = profile_entry(TRAFFIC_JSON, kernel_key)
+    return None if k is None else k["traffic_bytes"]
 
 
 def pick_tile(t256, batch, use, compute="bf16"):
@@ -891,6 +896,11 @@ def main():
     roof["kernel"] = dom_key
     roof["avg_launch_ms"] = round(dom["avg_launch_ms"], 4)
     roof["traffic"] = traffic_from_profiles(dom_key)
+    if bound == "mfma":
+        # fraction of cycles the matrix pipes were busy in this launch kind,
+        # from the committed MFMA counter summary (calibrated on the probe)
+        m = profile_entry(MFMA_JSON, dom_key)
+        roof["mfma_busy"] = None if m is None else round(m["mfma_busy_frac"], 3)
 
     # element-wise part: the optimizer state's own bytes per element (gradient
     # read, momentum read and written, weights read and written); prep moves

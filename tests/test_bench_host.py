@@ -107,3 +107,16 @@ def test_tile_table_marks_the_faster_tile(tmp_path, capsys):
     assert cells[4].endswith("✓") and cells[5].endswith("✓")   # 256 was faster
     assert not cells[6].endswith("✓")                  # update: 256 faster, 128 chosen
     assert not cells[7].endswith("✓")
+
+
+def test_counter_summaries_only_for_the_current_kernels(tmp_path):
+    # a summary keyed to other kernel sources is not used (null in the line)
+    good = {"kernel_source_sha256": bench.kernel_source_digest(),
+            "kernels": {"update_3072x12288": {"traffic_bytes": 1.0, "mfma_busy_frac": 0.5}}}
+    stale = dict(good, kernel_source_sha256="0" * 64)
+    for data, expect in ((good, 0.5), (stale, None)):
+        p = tmp_path / "summary.json"
+        p.write_text(json.dumps(data))
+        e = bench.profile_entry(str(p), "update_3072x12288")
+        assert (e["mfma_busy_frac"] if e else None) == expect
+    assert bench.profile_entry(str(tmp_path / "missing.json"), "update_3072x12288") is None
