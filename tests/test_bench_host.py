@@ -120,3 +120,27 @@ def test_counter_summaries_only_for_the_current_kernels(tmp_path):
         e = bench.profile_entry(str(p), "update_3072x12288")
         assert (e["mfma_busy_frac"] if e else None) == expect
     assert bench.profile_entry(str(tmp_path / "missing.json"), "update_3072x12288") is None
+
+
+def test_launch_sequence_groups_match_the_library():
+    # bench.py's model of the launch order groups matrices as the library's
+    # planner does: oriented shapes in order of first appearance, chunks of
+    # at most 64 (one prep launch each)
+    import dataclasses
+    import random
+    import muon_newton_schulz_step_amd as mn
+    rng = random.Random(11)
+    sides = (1, 64, 130, 300, 768, 1024, 2049)
+    for _ in range(40):
+        shapes = tuple((rng.choice(sides), rng.choice(sides)) for _ in range(rng.randint(1, 150)))
+        w = dataclasses.replace(wl.GPT_D768, shapes=shapes)
+        _, groups = mn.plan_groups(shapes)
+        seq = bench.launch_sequence(w)
+        order, preps = [], {}
+        for kind, m, n in seq:
+            if (m, n) not in preps:
+                order.append((m, n))
+                preps[(m, n)] = 0
+            preps[(m, n)] += kind == "prep"
+        assert order == [(m, n) for m, n, _ in groups]
+        assert [preps[(m, n)] for m, n, _ in groups] == [-(-c // 64) for _, _, c in groups]
