@@ -54,6 +54,23 @@ def test_step_mixed_shapes(compute, grad_dtype):
         check_matrix(w, inputs, k, before, bufs_before, compute)
 
 
+@pytest.mark.parametrize("n_steps", [1, 2, 3])
+@pytest.mark.parametrize("compute", ["bf16", "fp32"])
+def test_step_few_newton_schulz_steps(compute, n_steps):
+    """The first step is also the last (the normalisation folded into the
+    Gram and the weight update of one launch pair), two steps, and three,
+    whose step 1 forms the 2048x8192 group's Gram matrix as Q A Q on the
+    bf16 path."""
+    announce("few NS steps", compute, n_steps)
+    shapes = ((96, 256), (256, 96), (300, 700), (2048, 8192))
+    w = dataclasses.replace(wl.GPT_D768, shapes=shapes)
+    coeffs = w.coeff_table[:n_steps]
+    inputs = wl.make_inputs(w, device=DEV)
+    before, bufs_before = run_step(w, inputs, compute, coeffs=coeffs)
+    for k in range(len(shapes)):
+        check_matrix(w, inputs, k, before, bufs_before, compute, coeffs=coeffs)
+
+
 def test_step_final_parts_with_their_own_tiles():
     """One oriented chunk of 32 wide 512x2048 matrices and one tall 2048x512:
     the wide part's weight update runs on 256x256 tiles (512 of them), the
