@@ -62,9 +62,9 @@ def gpu_direction(w, inp, vs, indices, **call):
 
 
 def run_case(compute, wd, cautious, normuon, steps=1, shapes=SHAPES, beta2=0.9,
-             normuon_eps=1e-8):
-    announce("step_ex", compute, wd, cautious, normuon, steps)
-    w = dataclasses.replace(wl.GPT_D768, shapes=shapes)
+             normuon_eps=1e-8, ns_steps=5):
+    announce("step_ex", compute, wd, cautious, normuon, steps, ns_steps)
+    w = dataclasses.replace(wl.GPT_D768, shapes=shapes, n_steps=ns_steps)
     inp = wl.make_inputs(w, device=DEV)
     vs = [wl.make_second_moment(w, i, device=DEV) for i in range(len(shapes))] if normuon else None
     state = [dict(w=to64(inp["params"][k]), buf=to64(inp["bufs"][k]),
@@ -114,6 +114,13 @@ def test_normuon(compute):
 @pytest.mark.parametrize("compute", ["bf16", "fp32"])
 def test_normuon_with_cautious_decay_two_steps(compute):
     run_case(compute, wd=0.5, cautious=True, normuon=True, steps=2, beta2=0.75)
+
+
+@pytest.mark.parametrize("compute", ["bf16", "fp32"])
+def test_normuon_cautious_decay_one_newton_schulz_step(compute):
+    # the row statistics and the decay taken from the first step's update,
+    # which is also the last
+    run_case(compute, wd=0.5, cautious=True, normuon=True, ns_steps=1)
 
 
 def test_normuon_beta2_one_keeps_state_and_zero_eps():
