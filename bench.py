@@ -568,7 +568,7 @@ def measure_peaks(torch, mn, dev):
     src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
     copy_gbs = 0.0
-    for cblocks in (256 * 4, 256 * 8, 256 * 16, 256 * 32):
+    for cblocks in (256, 256 * 2, 256 * 4, 256 * 8, 256 * 16, 256 * 32):
         mn.probe_copy(src, dst, cblocks)  # warm-up
         e0.record(stream)
         moved = sum(mn.probe_copy(src, dst, cblocks) for _ in range(10))
@@ -580,7 +580,7 @@ def measure_peaks(torch, mn, dev):
             "how": "library probes on this GPU in this run: back-to-back "
                    "v_mfma_f32_32x32x16_bf16 on registers (1024 x 8 waves x 4 chains x "
                    "1e5 rounds, 3 launches); 2 GiB copy in 16-byte accesses, 4 loads in "
-                   "flight per thread (10 launches each at 1024-8192 workgroups, the best)"}
+                   "flight per thread (10 launches each at 256-8192 workgroups, the best)"}
 
 
 def measure_vendor_gemm(torch, dev, w):
