@@ -63,7 +63,7 @@ typedef struct { float a, b, c; } muon_coeff;
 typedef enum {
   MUON_OK = 0,
   MUON_ERR_INVALID_ARG = -1, /* null pointer, bad size, misalignment, aliasing */
-  MUON_ERR_UNSUPPORTED = -2, /* valid request this build does not implement */
+  MUON_ERR_UNSUPPORTED = -2, /* valid request the library does not implement */
   MUON_ERR_WORKSPACE = -3,   /* workspace missing, too small or misaligned */
   MUON_ERR_HIP = -4          /* a HIP launch or runtime call failed */
 } muon_status;

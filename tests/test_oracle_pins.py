@@ -390,7 +390,7 @@ def test_planted_normalisation_mistake_is_caught(monkeypatch):
     assert np.max(np.abs(o - spectral_closed_form(g, QUINTIC))) > 1e-3
 
 
-# ------------------------------ the comparison every parity verdict rests on
+# ------------------------------ the comparison every parity check rests on
 def _rfe_pins(rfe):
     """True if ``rfe`` passes every hand-computed case of the relative
     Frobenius error ||y - y_ref||_F / ||y_ref||_F."""
