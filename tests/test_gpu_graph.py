@@ -5,7 +5,8 @@ eagerly, bitwise (the kernels are deterministic); replays reuse the captured
 arguments (lr, mu, scales, coefficients).  Two sets: small chunks that run
 concurrently on library lanes (forked off the captured stream and joined
 back to it), and a large chunk beside a small one, which run in turn on the
-captured stream."""
+captured stream; and muon_step_ex with NorMuon and cautious decay, whose
+row-statistics and weight passes are captured the same way."""
 import dataclasses
 
 import pytest
@@ -51,5 +52,44 @@ def test_captured_step_replays_match_eager(compute, which):
         for x, y in zip(a["params"] + a["bufs"], b["params"] + b["bufs"]):
             assert torch.equal(x, y), replay
         # unrelated eager work between replays
+        torch.randn(1 << 20, device=DEV).square().sum().item()
+    del g
+
+
+@pytest.mark.parametrize("compute", ["bf16", "fp32"])
+def test_captured_step_ex_replays_match_eager(compute):
+    # NorMuon with cautious decay: the row-statistics and weight passes are
+    # launches too, so the captured step replays like the plain one
+    import ctypes
+    from muon_newton_schulz_step_amd import _lib
+    announce("graph capture step_ex", compute)
+    w = dataclasses.replace(wl.GPT_D768, shapes=SETS["concurrent"])
+    a = wl.make_inputs(w, device=DEV)
+    b = wl.make_inputs(w, device=DEV)
+    va = [wl.make_second_moment(w, i, device=DEV) for i in range(len(w.shapes))]
+    vb = [v.clone() for v in va]
+    opt = dict(weight_decay=0.1, cautious=True, beta2=0.95, normuon_eps=1e-8)
+    o = _lib.MuonOptions(0.1, 1, 1, 0.95, 1e-8)
+    need = mn.lib().muon_step_ex_workspace_bytes(
+        len(w.shapes), _lib.int_array([r for r, _ in w.shapes]),
+        _lib.int_array([c for _, c in w.shapes]), 0 if compute == "bf16" else 1, ctypes.byref(o))
+    assert need > 0
+    ws_a = torch.empty(need, dtype=torch.uint8, device=DEV)
+    ws_b = torch.empty(need, dtype=torch.uint8, device=DEV)
+    kw = dict(mu=w.mu, lr=w.lr, coeffs=w.coeff_table, compute=compute, **opt)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mn.step_ex(a["params"], a["grads"], a["bufs"], scales=a["scales"], second_moments=va,
+                   workspace=ws_a, **kw)
+    torch.cuda.synchronize()
+    for x, y in zip(a["params"] + a["bufs"] + va, b["params"] + b["bufs"] + vb):
+        assert torch.equal(x, y)  # capturing ran nothing
+    for replay in range(3):
+        g.replay()
+        mn.step_ex(b["params"], b["grads"], b["bufs"], scales=b["scales"], second_moments=vb,
+                   workspace=ws_b, **kw)
+        torch.cuda.synchronize()
+        for x, y in zip(a["params"] + a["bufs"] + va, b["params"] + b["bufs"] + vb):
+            assert torch.equal(x, y), replay
         torch.randn(1 << 20, device=DEV).square().sum().item()
     del g
