@@ -5,8 +5,9 @@ eagerly, bitwise (the kernels are deterministic); replays reuse the captured
 arguments (lr, mu, scales, coefficients).  Two sets: small chunks that run
 concurrently on library lanes (forked off the captured stream and joined
 back to it), and a large chunk beside a small one, which run in turn on the
-captured stream; and muon_step_ex with NorMuon and cautious decay, whose
-row-statistics and weight passes are captured the same way."""
+captured stream; muon_step_ex with NorMuon and cautious decay, whose
+row-statistics and weight passes are captured the same way; and the
+allocation-free muon_step_static beside muon_orthogonalize in one graph."""
 import dataclasses
 
 import pytest
@@ -91,5 +92,34 @@ def test_captured_step_ex_replays_match_eager(compute):
         torch.cuda.synchronize()
         for x, y in zip(a["params"] + a["bufs"] + va, b["params"] + b["bufs"] + vb):
             assert torch.equal(x, y), replay
+        torch.randn(1 << 20, device=DEV).square().sum().item()
+    del g
+
+
+def test_captured_static_step_and_orthogonalize_replay():
+    # the allocation-free entry point (its scratch is the library's own) and
+    # orthogonalize with a caller workspace, captured and replayed likewise
+    announce("graph capture static step and orthogonalize")
+    w = dataclasses.replace(wl.GPT_D768, shapes=SETS["concurrent"])
+    a = wl.make_inputs(w, device=DEV)
+    b = wl.make_inputs(w, device=DEV)
+    x = wl.gaussian_batch(3, 300, 700, seed=12, device=DEV)
+    oa = torch.empty_like(x)
+    ws = torch.empty(mn.orthogonalize_workspace_bytes(3, 300, 700, "bf16"), dtype=torch.uint8,
+                     device=DEV)
+    kw = dict(mu=w.mu, lr=w.lr, coeffs=w.coeff_table, compute="bf16")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mn.step_static(a["params"], a["grads"], a["bufs"], scales=a["scales"], **kw)
+        mn.orthogonalize(x, w.coeff_table, compute="bf16", out=oa, workspace=ws)
+    torch.cuda.synchronize()
+    for replay in range(3):
+        g.replay()
+        mn.step_static(b["params"], b["grads"], b["bufs"], scales=b["scales"], **kw)
+        ob = mn.orthogonalize(x, w.coeff_table, compute="bf16")
+        torch.cuda.synchronize()
+        for p, q in zip(a["params"] + a["bufs"], b["params"] + b["bufs"]):
+            assert torch.equal(p, q), replay
+        assert torch.equal(oa, ob), replay
         torch.randn(1 << 20, device=DEV).square().sum().item()
     del g
