@@ -114,3 +114,53 @@ def test_two_streams_with_default_workspaces():
             assert torch.equal(x, y)
     keys = [k for k in mn._default_ws if k[0] == "cuda:0"]
     assert len({k[1] for k in keys}) >= 2
+
+
+def test_host_threads_stepping_at_once():
+    """Four host threads, each with its own stream and workspace, step
+    small sets whose chunks run on the library's shared stream lanes (the
+    ctypes calls release the interpreter lock, so the library's entry points
+    run at the same time): every result equals, bitwise, the same step run
+    alone."""
+    import threading
+    announce("four host threads")
+    w = dataclasses.replace(wl.GPT_D768, shapes=((96, 256), (256, 96), (128, 128), (300, 700)))
+    sets = [wl.make_inputs(dataclasses.replace(w, seed=w.seed + 7 * t), device="cuda:0")
+            for t in range(4)]
+    need = mn.step_workspace_bytes(w.shapes, "bf16")
+    expect = []
+    for inp in sets:
+        p = [x.clone() for x in inp["params"]]
+        b = [x.clone() for x in inp["bufs"]]
+        for _ in range(3):
+            mn.step(p, inp["grads"], b, mu=w.mu, lr=w.lr, scales=inp["scales"],
+                    coeffs=w.coeff_table, workspace=torch.empty(need, dtype=torch.uint8,
+                                                                device="cuda:0"))
+        torch.cuda.synchronize()
+        expect.append(p + b)
+    streams = [torch.cuda.Stream() for _ in sets]
+    wss = [torch.empty(need, dtype=torch.uint8, device="cuda:0") for _ in sets]
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(t):
+        try:
+            inp, s = sets[t], streams[t]
+            with torch.cuda.stream(s):
+                for _ in range(3):
+                    mn.step(inp["params"], inp["grads"], inp["bufs"], mu=w.mu, lr=w.lr,
+                            scales=inp["scales"], coeffs=w.coeff_table, workspace=wss[t])
+            s.synchronize()
+        except Exception as e:  # noqa: BLE001 - reported below
+            errors.append(e)
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=120)
+    assert not any(th.is_alive() for th in threads)
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for inp, exp in zip(sets, expect):
+        for x, y in zip(inp["params"] + inp["bufs"], exp):
+            assert torch.equal(x, y)
