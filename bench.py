@@ -61,6 +61,9 @@ def parse():
     p.add_argument("--matrices", type=int, default=None,
                    help="time a bounded sample: the first N matrices of each raw shape of "
                         "the workload")
+    p.add_argument("--owner-share", type=int, default=None, metavar="N",
+                   help="time the matrices one rank owns in an N-way step sharded by whole "
+                        "matrix (every N-th matrix of each oriented shape)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--graph", action="store_true",
                    help="time replays of one captured step (a HIP graph: no per-launch host "
@@ -774,14 +777,20 @@ def main():
         return
     w = wl.WORKLOADS[args.workload]
     full_count = len(w.shapes)
-    if args.coeffs or args.ns_steps or args.matrices:
+    if args.owner_share is not None and (args.owner_share < 1 or args.matrices):
+        print("--owner-share takes N >= 1 and does not combine with --matrices",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.coeffs or args.ns_steps or args.matrices or args.owner_share:
         import dataclasses
         w = dataclasses.replace(
             w, coeffs={"quintic": wl.QUINTIC, "cubic": wl.CUBIC}[args.coeffs or "quintic"]
             if args.coeffs else w.coeffs,
             n_steps=args.ns_steps or w.n_steps,
             shapes=(tuple(w.shapes[i] for i in wl.sample_indices(w, args.matrices))
-                    if args.matrices else w.shapes))
+                    if args.matrices else
+                    tuple(w.shapes[i] for i in wl.owner_indices(w, args.owner_share))
+                    if args.owner_share else w.shapes))
     if args.write_traffic:
         write_traffic(args.write_traffic[0], args.write_traffic[1], w)
         return
@@ -946,13 +955,18 @@ def main():
         "dtype": args.compute,
         "data": "synthetic (seeded, generated on the GPU)",
         "config": {"workload": w.name, "matrices": len(w.shapes),
-                   **({"sample_of": full_count} if len(w.shapes) != full_count else {}),
+                   **({"owner_share": f"rank 0 of {args.owner_share}", "of": full_count}
+                      if args.owner_share else
+                      {"sample_of": full_count} if len(w.shapes) != full_count else {}),
                    "variant": args.variant,
                    **({"options": opt} if opt else {}),
                    "oriented_groups": {f"{m}x{n}": c for (m, n), c in groups.items()},
                    "ns_steps": w.n_steps, "coeffs": list(w.coeffs),
                    "launch": "hip graph replay" if args.graph else "eager",
-                   "parallelism": f"single GPU, all {len(w.shapes)} matrices of the set"},
+                   "parallelism": (f"single GPU: the {len(w.shapes)} matrices that one rank "
+                                   f"owns in a {args.owner_share}-way step sharded by whole "
+                                   f"matrix" if args.owner_share else
+                                   f"single GPU, all {len(w.shapes)} matrices of the set")},
         "ns_tflops": round(ns_tflops, 2),
         "ns_ms_per_step": round(ns_ms, 3),
         "ns_frac_of_peak": round(ns_tflops / PEAK[args.compute], 4),

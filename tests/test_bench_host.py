@@ -19,6 +19,14 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in out.stderr and out.stdout == ""
 
 
+def test_bad_owner_share_is_refused():
+    for extra in (["--owner-share", "0"], ["--owner-share", "8", "--matrices", "2"]):
+        out = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *extra],
+                             capture_output=True, text=True, timeout=120, cwd=ROOT)
+        assert out.returncode == 2, extra
+        assert "--owner-share" in out.stderr and out.stdout == ""
+
+
 def test_launch_sequence_of_the_3p8b_step():
     seq = bench.launch_sequence(wl.GPT_3P8B)
     groups = {}

@@ -3,6 +3,7 @@ import dataclasses
 import math
 
 import numpy as np
+import pytest
 import torch
 
 import workloads as wl
@@ -72,3 +73,25 @@ def test_ragged_helpers():
     assert a.shape == (3, 5, 7)
     assert torch.equal(a[0], wl.gaussian_batch(1, 5, 7, seed=1)[0])
     assert wl.sample_indices(wl.GPT_3P8B, 2) == [0, 1, 2, 3, 4, 5, 10, 11]
+
+
+def test_owner_indices_partition_every_oriented_group():
+    """Sharding by whole matrix: over n ranks every matrix has exactly one
+    owner, and each rank holds 1/n of every oriented group (the 3.8B set's
+    groups of 56: 7 each on 8 ranks)."""
+    w = wl.GPT_3P8B
+    owners = {}
+    for rank in range(8):
+        idx = wl.owner_indices(w, 8, rank)
+        groups = {}
+        for i in idx:
+            assert i not in owners
+            owners[i] = rank
+            r, c = w.shapes[i]
+            groups[(min(r, c), max(r, c))] = groups.get((min(r, c), max(r, c)), 0) + 1
+        assert groups == {(3072, 3072): 7, (1024, 3072): 7, (3072, 12288): 7}
+    assert sorted(owners) == list(range(len(w.shapes)))
+    assert wl.owner_indices(w, 1) == list(range(len(w.shapes)))
+    for bad in ((0, 0), (8, 8), (8, -1)):
+        with pytest.raises(ValueError):
+            wl.owner_indices(w, *bad)

@@ -234,6 +234,25 @@ def sample_indices(w: Workload, per_group: int):
     return out
 
 
+def owner_indices(w: Workload, n_ranks: int, rank: int = 0):
+    """Matrices that ``rank`` owns when the step is sharded by whole matrix
+    over ``n_ranks`` GPUs: within every oriented shape (min and max of rows
+    and cols), every ``n_ranks``-th matrix in list order, starting at
+    ``rank``.  Each rank then runs the same oriented groups, 1/n_ranks as
+    large (the 3.8B set's groups of 56 give 7 per rank on 8)."""
+    if n_ranks < 1 or not 0 <= rank < n_ranks:
+        raise ValueError("need n_ranks >= 1 and 0 <= rank < n_ranks")
+    pos: dict = {}
+    out = []
+    for i, (r, c) in enumerate(w.shapes):
+        key = (min(r, c), max(r, c))
+        k = pos.get(key, 0)
+        pos[key] = k + 1
+        if k % n_ranks == rank:
+            out.append(i)
+    return out
+
+
 def gaussian_matrix(rows: int, cols: int, seed: int, device="cpu",
                     dtype=torch.float32, std: float = 1.0) -> torch.Tensor:
     """A seeded N(0, std) matrix for the ragged/edge-shape parity cases."""
