@@ -41,6 +41,10 @@
  *    (default priority), forked off the caller's stream with an event and
  *    joined back to it before the call returns, so stream order and graph
  *    capture see one step as usual.
+ *  - The step entry points (muon_step, muon_step_ex, muon_step_static) work
+ *    on the calling thread's current device, whose library streams and
+ *    static scratch they use: a `stream` that belongs to another device
+ *    returns MUON_ERR_INVALID_ARG before anything is enqueued.
  */
 #ifndef MUON_H
 #define MUON_H

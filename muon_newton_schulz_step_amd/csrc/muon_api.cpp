@@ -618,6 +618,20 @@ Lanes* lanes_of_current_device() {
   return &L;
 }
 
+// The stream lanes of a concurrent step and the allocation-free entry
+// point's scratch belong to the calling thread's current device, so a step
+// refuses a stream of another device (MUON_ERR_INVALID_ARG, nothing
+// enqueued).  A handle the runtime cannot attribute to a device (the null
+// stream, special handles) passes; a bad one fails at its first launch.
+int check_stream_device(hipStream_t stream) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return MUON_ERR_HIP;
+  hipDevice_t own = -1;
+  if (stream != nullptr && hipStreamGetDevice(stream, &own) == hipSuccess && own != cur)
+    return MUON_ERR_INVALID_ARG;
+  return MUON_OK;
+}
+
 int check_options(const muon_options* o) {
   if (!o) return MUON_OK;
   if (!is_finite(o->weight_decay) || o->weight_decay < 0.f) return MUON_ERR_INVALID_ARG;
@@ -713,6 +727,8 @@ int step_impl(int n, const int* rows, const int* cols, void* const* params, int 
                             (size_t)(rows[i] < cols[i] ? rows[i] : cols[i]) * 4)))
       return MUON_ERR_INVALID_ARG;
   }
+
+  if (int st = check_stream_device(stream)) return st;
 
   const bool cbf16 = compute == MUON_BF16;
   std::vector<Group> groups;

@@ -319,3 +319,36 @@ def test_shared_gradient_and_aliasing_refused():
     torch.cuda.synchronize()
     for x, y in zip(a["params"], kept):
         assert torch.equal(x, y)
+
+
+@pytest.mark.skipif(torch.cuda.device_count() < 2, reason="needs a second GPU for a stream "
+                    "that belongs to another device")
+def test_stream_of_another_device_refused():
+    """The step works on the calling thread's current device (its stream
+    lanes and static scratch live there): with device 0 current, a stream of
+    device 1 returns MUON_ERR_INVALID_ARG and nothing is written."""
+    announce("stream of another device")
+    from muon_newton_schulz_step_amd import _lib
+    torch.cuda.set_device(0)
+    rows, cols = 64, 128
+    p = torch.zeros(rows, cols, device=DEV)
+    g = torch.ones(rows, cols, device=DEV, dtype=torch.bfloat16)
+    b = torch.zeros(rows, cols, device=DEV)
+    lib = mn.lib()
+    need = lib.muon_step_workspace_bytes(1, _lib.int_array([rows]), _lib.int_array([cols]), 0)
+    ws = torch.empty(need + 256, dtype=torch.uint8, device=DEV)
+    wp = (ws.data_ptr() + 255) // 256 * 256
+    other = torch.cuda.Stream(device=1)
+    for call in (lambda s: lib.muon_step(
+            1, _lib.int_array([rows]), _lib.int_array([cols]), _lib.ptr_array([p.data_ptr()]),
+            _lib.MUON_FP32, _lib.ptr_array([g.data_ptr()]), _lib.MUON_BF16,
+            _lib.ptr_array([b.data_ptr()]), 0.95, 0.02, _lib.float_array([1.0]),
+            _lib.coeff_array([wl.QUINTIC] * 5), 5, 1e-7, 0, wp, need, s),
+                 lambda s: lib.muon_step_static(
+            1, _lib.int_array([rows]), _lib.int_array([cols]), _lib.ptr_array([p.data_ptr()]),
+            _lib.MUON_FP32, _lib.ptr_array([g.data_ptr()]), _lib.MUON_BF16,
+            _lib.ptr_array([b.data_ptr()]), 0.95, 0.02, _lib.float_array([1.0]),
+            _lib.coeff_array([wl.QUINTIC] * 5), 5, 1e-7, 0, s)):
+        assert call(other.cuda_stream) == _lib.MUON_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert torch.all(p == 0) and torch.all(b == 0)
