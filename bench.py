@@ -92,6 +92,9 @@ def parse():
     p.add_argument("--overlap-probe", action="store_true",
                    help="run the library's MFMA probe and copy probe alone and side by side "
                         "on two streams (one long launch each) and print what each sustains")
+    p.add_argument("--batch-sweep", action="store_true",
+                   help="time each GEMM kind of one orthogonalisation against the batch size "
+                        "(launch time against tile count: rounds of the CUs or a straight line)")
     p.add_argument("--write-mfma", metavar="MFMA_CSV",
                    help="turn a rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 "
                         "SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE counter CSV of a "
@@ -677,6 +680,75 @@ def tile_sweep(torch, mn, wl, reps=11):
         torch.cuda.empty_cache()
 
 
+# (rows, cols, batches): the 3.8B set's square and wide groups around 56
+# matrices (4368 lower-triangle tiles of 256 = 17.06 rounds of the 256 CUs),
+# and the d768 set's wide group, whose launches hold a few rounds only.
+BATCH_SWEEP_SETS = ((3072, 3072, (48, 52, 54, 55, 56, 57, 58, 60, 64)),
+                    (3072, 12288, (52, 55, 56, 57)),
+                    (768, 3072, (8, 12, 16, 20, 24, 32)))
+
+
+def batch_sweep(torch, mn, reps=3):
+    """For each set, one JSON line per batch with the median launch time of
+    each GEMM kind over `reps` bf16 orthogonalisations (HIP events of the
+    library), then one line per kind with two fits of launch time against
+    the batch: a straight line (time proportional to the tiles) and a
+    multiple of the rounds of 256 workgroups the launch needs (time set by
+    whole rounds), each with its largest relative residual."""
+    import numpy as np
+    dev = "cuda:0"
+    for rows, cols, batches in BATCH_SWEEP_SETS:
+        per_batch = {}
+        for batch in batches:
+            g = torch.Generator(device=dev).manual_seed(batch)
+            x = (torch.randn(batch, rows, cols, device=dev, generator=g) * 1e-3).to(torch.bfloat16)
+            out = torch.empty_like(x)
+            mn.orthogonalize(x, out=out)
+            torch.cuda.synchronize()
+            mn.timing_enable(True)
+            mn.timing_read()
+            for _ in range(reps):
+                mn.orthogonalize(x, out=out)
+            torch.cuda.synchronize()
+            mn.timing_enable(False)
+            per = {}
+            for rec in mn.timing_read():
+                if rec["kind"] in ("gram", "poly", "update", "gramq"):
+                    per.setdefault(rec["kind"], []).append(rec["ms"])
+            kinds = {k: round(float(np.median(v)), 4) for k, v in per.items()}
+            per_batch[batch] = kinds
+            print(json.dumps({"rows": rows, "cols": cols, "batch": batch, "kinds": kinds}),
+                  flush=True)
+            del x, out
+            torch.cuda.empty_cache()
+        t256, n256 = -(-rows // 256), -(-cols // 256)
+        for kind in sorted({k for v in per_batch.values() for k in v}):
+            bs = np.array([b for b in batches if kind in per_batch[b]], dtype=float)
+            ms = np.array([per_batch[int(b)][kind] for b in bs])
+            full = kind == "update"
+            per256 = t256 * n256 if full else t256 * (t256 + 1) // 2
+            per128 = 4 * t256 * n256 if full else (2 * t256) * (2 * t256 + 1) // 2
+            tiles = bs * per256
+            tile = [pick_tile(t256 * n256 if full else t256, int(b),
+                              "full" if full else "gram" if kind == "gram" else "tri")
+                    for b in bs]
+            line = np.polyfit(bs, ms, 1)
+            res_line = np.abs(np.polyval(line, bs) - ms) / ms
+            # whole rounds: 256 workgroups of 256-tiles, or 512 of 128-tiles
+            rounds = np.array([-(-int(b) * per256 // 256) if tl == 256
+                               else -(-int(b) * per128 // 512)
+                               for b, tl in zip(bs, tile)], dtype=float)
+            per_round = float(np.dot(rounds, ms) / np.dot(rounds, rounds))
+            res_round = np.abs(rounds * per_round - ms) / ms
+            print(json.dumps({"rows": rows, "cols": cols, "kind": kind,
+                              "tiles_256": [int(t) for t in tiles], "tile": tile,
+                              "line_ms": [round(float(line[1]), 4), round(float(line[0]), 5)],
+                              "line_max_rel_residual": round(float(res_line.max()), 4),
+                              "ms_per_round": round(per_round, 4),
+                              "rounds_max_rel_residual": round(float(res_round.max()), 4)}),
+                  flush=True)
+
+
 def overlap_probe(torch, mn, copy_gib=32, reps=2):
     """The two probes alone, then the copy launched first and the MFMA probe
     right after it on a second stream, so both run on the same CUs: one JSON
@@ -771,6 +843,9 @@ def main():
         return
     if args.tile_sweep:
         tile_sweep(torch, mn, wl)
+        return
+    if args.batch_sweep:
+        batch_sweep(torch, mn)
         return
     if args.overlap_probe:
         overlap_probe(torch, mn)
