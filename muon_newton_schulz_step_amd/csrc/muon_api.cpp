@@ -91,7 +91,8 @@ int pick_tile(bool cbf16, long long t256, int batch, TileUse use) {
 
 // Workspace regions for `cnt` matrices of oriented shape m x n (padded
 // M x N), the X state as described for PrepArgs:
-//   bf16: hi plane twice (the update reads one, writes the other), lo plane;
+//   bf16: hi plane twice (the update reads one, writes the other), lo plane
+//         (one byte per element);
 //   fp32: X, X^T twice (read by the update, written by it).
 // Then A and B (M x M, compute precision), the norm partials and 1/norm,
 // and with NorMuon the per-row scales 1/(sqrt(v') + eps) (M floats) and, on
@@ -123,13 +124,14 @@ bool qaq_step(int k, int n_steps) { return (k == 1 || k == 3) && k <= n_steps - 
 // epilogues and prep load and store the X state, weights, gradient and
 // momentum nontemporally, which leaves L2 to the GEMM operand panels.
 // Smaller ones keep X cached for the next launch.  (The d768 GPT set, two
-// concurrent chunks of 113 and 226 MB: 1.67 ms cached, 1.57 ms streamed.)
+// concurrent chunks of 94 and 189 MB: 1.67 ms cached, 1.57 ms streamed,
+// measured with a 2-byte lo plane, when they held 113 and 226 MB.)
 constexpr double kStreamBytes = 256.0 * (1 << 20);
 
 // X-state bytes of a chunk of `cnt` matrices of oriented shape m x n:
-// bf16 hi twice + lo, fp32 X + X^T twice.
+// bf16 hi twice + the one-byte lo, fp32 X + X^T twice.
 double x_state_bytes(int cnt, int m, int n, bool cbf16) {
-  return (double)cnt * (double)pad_dim(m) * (double)pad_dim(n) * (cbf16 ? 6.0 : 12.0);
+  return (double)cnt * (double)pad_dim(m) * (double)pad_dim(n) * (cbf16 ? 5.0 : 12.0);
 }
 
 bool make_layout(int cnt, int m, int n, bool cbf16, Layout& L, bool normuon = false) {
@@ -147,7 +149,7 @@ bool make_layout(int cnt, int m, int n, bool cbf16, Layout& L, bool normuon = fa
   };
   L.x0 = take((size_t)cnt * MN * es);  // bf16: hi 0   fp32: X
   L.x1 = take((size_t)cnt * MN * es);  // bf16: hi 1   fp32: X^T 0
-  L.x2 = take((size_t)cnt * MN * es);  // bf16: lo     fp32: X^T 1
+  L.x2 = take((size_t)cnt * MN * (cbf16 ? 1 : 4));  // bf16: lo (1 byte)  fp32: X^T 1
   L.A = take((size_t)cnt * MM * es);
   L.B = take((size_t)cnt * MM * es);
   L.qaq = gram_by_qaq(cbf16, M, N);
@@ -275,9 +277,9 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
     pa.Xf = Xf; pa.XT = XT[0]; pa.sXT = MN;
   }
   pa.partials = part; pa.nblk = L.nblk;
-  // reads g (and momentum r/w); writes X_0: hi + lo, or X + X^T
+  // reads g (and momentum r/w); writes X_0: hi + lo (3 bytes), or X + X^T
   const double gsz = c.in_bf16 ? 2 : 4;
-  const double prep_bytes = elems * (gsz + (c.momentum ? 8.0 : 0.0)) + pmn * (cbf16 ? 4.0 : 8.0);
+  const double prep_bytes = elems * (gsz + (c.momentum ? 8.0 : 0.0)) + pmn * (cbf16 ? 3.0 : 8.0);
   hipError_t err = timed(MUON_K_PREP, L.m, L.n, c.cnt, -1, 0.0, 0.0, prep_bytes, s, [&] {
     return launch_prep(c.in_bf16, cbf16, c.momentum, pa, c.pt, c.cnt, s);
   });
@@ -401,8 +403,8 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
         g.ld_rp = L.M;
         g.s_rp = (long long)(L.N / 64) * L.M;
       }
-      const double upd_bytes = pmm * es + pmn * es + pmn * 4.0 + pmn * (cbf16 ? 4.0 : 8.0) +
-                               (rows ? pmn / 16.0 : 0.0);
+      const double upd_bytes = pmm * es + pmn * es + pmn * (cbf16 ? 3.0 : 4.0) +
+                               pmn * (cbf16 ? 3.0 : 8.0) + (rows ? pmn / 16.0 : 0.0);
       err = timed(MUON_K_UPDATE, L.m, L.n, c.cnt, k, cnt * 2.0 * m * m * n, cnt * x_upd, upd_bytes,
                   s, [&] {
         return launch_gemm(cbf16, rows ? EPI_UPDATE_ROWS : EPI_UPDATE, tile_upd, g, c.wt, c.cnt, s);
@@ -431,7 +433,7 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
                         : c.final_mode == FINAL_WEIGHTS ? (part ? EPI_FINAL_W_T : EPI_FINAL_W)
                                                         : (part ? EPI_FINAL_OUT_T : EPI_FINAL_OUT);
         const double bm = b, pmn_b = bm * (double)MN, el_b = m * n * bm;
-        const double fin_bytes = bm * (double)MM * es + pmn_b * es + pmn_b * 4.0 +
+        const double fin_bytes = bm * (double)MM * es + pmn_b * es + pmn_b * (cbf16 ? 3.0 : 4.0) +
                                  (c.final_mode == FINAL_WEIGHTS ? el_b * 8.0
                                                                 : el_b * (c.out_bf16 ? 2.0 : 4.0));
         err = timed(MUON_K_FINAL, L.m, L.n, b, k, bm * 2.0 * m * m * n, bm * x_upd, fin_bytes, s,
@@ -467,7 +469,7 @@ int run_chunk(const Chunk& c, const Layout& L, char* ws, const muon_coeff* coeff
     aa.Xh = Xh[n_steps & 1]; aa.Xl = Xl; aa.Xf = Xf;
     aa.rinv = rinv;
     aa.neg_lr = c.neg_lr; aa.neg_lrwd = c.neg_lrwd; aa.cautious = c.cautious;
-    err = timed(MUON_K_APPLY, L.m, L.n, c.cnt, -1, 0.0, 0.0, elems * 12.0, s,
+    err = timed(MUON_K_APPLY, L.m, L.n, c.cnt, -1, 0.0, 0.0, elems * (cbf16 ? 11.0 : 12.0), s,
                 [&] { return launch_apply(cbf16, aa, c.wt, c.cnt, s); });
     if (err != hipSuccess) return MUON_ERR_HIP;
   }

@@ -43,10 +43,48 @@ __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
 }
 
 // x as the sum of two bf16 values: hi = bf16(x), lo = bf16(x - hi) (the
-// difference is exact in fp32), 16 significant bits in all.
+// difference is exact in fp32), 16 significant bits in all.  (A's residual
+// in the Q A Q Gram steps.)
 __device__ __forceinline__ void split_bf16(float x, bf16_t& hi, bf16_t& lo) {
   hi = from_f32<bf16_t>(x);
   lo = from_f32<bf16_t>(x - to_f32(hi));
+}
+
+// The X state of the bf16 path between Newton-Schulz steps: hi = bf16(x) and
+// one signed byte q, x - hi in units of 1/256 of hi's bf16 spacing (ulp(hi):
+// 2^(e - 134) for hi's exponent field e, the smallest normal binade's for a
+// zero or subnormal hi):
+//   q = round((x - hi) * 256 / ulp(hi)), clamped to [-128, 127],
+//   x = hi + q * ulp(hi) / 256 to within ulp(hi) / 512,
+// 16 significant bits, as hi + bf16(x - hi) would hold, in 3 bytes instead
+// of 4.  |x - hi| <= ulp(hi) / 2, so only q = 128 is clamped (x - hi within
+// ulp/512 below +ulp/2, about one element in 512; error up to ulp/256).  A
+// non-finite hi (or |hi| >= 2^127) keeps q = 0; x comes back as NaN where hi
+// is not finite (0 * inf), as hi + bf16(x - hi) did.
+__device__ __forceinline__ unsigned lo8_exp(float hi) {
+  const unsigned e = (__float_as_uint(hi) >> 23) & 0xffu;
+  return e < 1u ? 1u : e;
+}
+// ulp(hi) / 256 = 2^(e - 127) * 2^-15
+__device__ __forceinline__ float lo8_unit(float hi) {
+  return __uint_as_float(lo8_exp(hi) << 23) * 0x1p-15f;
+}
+// q of x (hi = bf16(x)), as the byte's bit pattern in bits 0..7
+__device__ __forceinline__ unsigned lo8_of(float x, float hi) {
+  const unsigned e = lo8_exp(hi);
+  // (x - hi) / 2^(e - 142) = (x - hi) * 2^(127 - e) * 2^15, both factors exact
+  const float inv = e < 254u ? __uint_as_float((254u - e) << 23) : 0.f;
+  const float q = __builtin_rintf((x - hi) * inv * 32768.f);
+  const int qi = (int)__builtin_fminf(__builtin_fmaxf(q, -128.f), 127.f);
+  return (unsigned)qi & 0xffu;
+}
+// x from hi and the signed byte q
+__device__ __forceinline__ float lo8_x(float hi, int q) {
+  return __builtin_fmaf((float)q, lo8_unit(hi), hi);
+}
+// the signed byte b (0..3) of a packed word
+__device__ __forceinline__ int lo8_byte(unsigned w, int b) {
+  return (int)(w << (24 - 8 * b)) >> 24;
 }
 
 // One weight element: W' = W + wscale*x (wscale = -lr*scale, x the update

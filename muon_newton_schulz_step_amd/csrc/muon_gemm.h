@@ -486,13 +486,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
   float* __restrict__ Xf = nullptr;
   const bf16_t* __restrict__ Xh = nullptr;
   bf16_t* __restrict__ Xh_next = nullptr;
-  bf16_t* __restrict__ Xl = nullptr;
+  unsigned char* __restrict__ Xl = nullptr;  // one signed byte per element (lo8_of)
   float* __restrict__ W = nullptr;
   float wscale = 0.f;
   if constexpr (UPD || FINAL) {
     if constexpr (HILO) {
       Xh = static_cast<const bf16_t*>(a.Xh) + (long long)mat * a.sX;
-      Xl = static_cast<bf16_t*>(a.Xl) + (long long)mat * a.sX;
+      Xl = static_cast<unsigned char*>(a.Xl) + (long long)mat * a.sX;
       if constexpr (UPD)
         Xh_next = static_cast<bf16_t*>(a.Xh_next) + (long long)mat * a.sX;
     } else {
@@ -527,7 +527,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
       static_assert((size_t)NCH * 16 <= (QROW ? (size_t)STAGE * 16 : LDS_BYTES), "staging fits");
       float* __restrict__ Tf = QROW ? reinterpret_cast<float*>(S0) : reinterpret_cast<float*>(smem);
       // bf16 path: the block's X state (its SR rows, all BN columns) arrives
-      // as 16-byte runs of 8 columns of hi and lo, coalesced, and waits in
+      // as runs of 8 columns (16 bytes of hi, 8 of lo), coalesced, and waits in
       // the other stage as fp32 rows (columns of rows with bit 2 set XOR 32,
       // so the two half-waves' reads below hit different banks); the next
       // block's runs are loaded during this block's write-back.
@@ -540,7 +540,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
       auto xs_at = [](int il, int jl) __attribute__((always_inline)) {
         return il * BN + (jl ^ (((il >> 2) & 1) << 5));
       };
-      [[maybe_unused]] u32x4_t hv[HILO ? RPT : 1], lv[HILO ? RPT : 1];
+      [[maybe_unused]] u32x4_t hv[HILO ? RPT : 1];
+      [[maybe_unused]] u32x2_t lv[HILO ? RPT : 1];
       auto xload = [&](int mi) __attribute__((always_inline)) {
 #pragma unroll
         for (int s = 0; s < RPT; ++s) {
@@ -548,7 +549,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
           const long long o =
               (long long)(ti * BM + (il / 32) * WTM + mi * 32 + il % 32) * a.ldx + tj * BN + 8 * jr;
           hv[s] = ldx(reinterpret_cast<const u32x4_t*>(Xh + o));
-          lv[s] = ldx(reinterpret_cast<const u32x4_t*>(Xl + o));
+          lv[s] = ldx(reinterpret_cast<const u32x2_t*>(Xl + o));
         }
       };
       auto xstore = [&]() __attribute__((always_inline)) {
@@ -558,9 +559,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
           float x[8];
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
-            const unsigned hw = hv[s][w], lw = lv[s][w];
-            x[2 * w] = __uint_as_float(hw << 16) + __uint_as_float(lw << 16);
-            x[2 * w + 1] = __uint_as_float(hw & 0xffff0000u) + __uint_as_float(lw & 0xffff0000u);
+            const unsigned hw = hv[s][w], lw = lv[s][w / 2];
+            x[2 * w] = lo8_x(__uint_as_float(hw << 16), lo8_byte(lw, 2 * (w % 2)));
+            x[2 * w + 1] = lo8_x(__uint_as_float(hw & 0xffff0000u), lo8_byte(lw, 2 * (w % 2) + 1));
           }
           float* d = Xs + xs_at(il, 8 * jr);
           *reinterpret_cast<f32x4_t*>(d) = f32x4_t{x[0], x[1], x[2], x[3]};
@@ -679,8 +680,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
   }
 
   // UPDATE and the FINAL of wide matrices on the bf16 path: X's hi and lo
-  // planes move in runs of 8 consecutive columns (16-byte accesses, 8 lanes
-  // per 128-byte row segment) instead of one 2-byte element per lane and
+  // planes move in runs of 8 consecutive columns (16-byte hi and 8-byte lo
+  // accesses, 8 lanes per row segment) instead of one element per lane and
   // access, and so do the weights (or the output) where their rows are
   // 16-byte aligned (vec_wide), element by element at ragged edges.  Each wave writes its
   // accumulators of one 32-row block as fp32 rows into its own LDS area and
@@ -705,12 +706,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
     auto offset = [&](int mi, int s) __attribute__((always_inline)) {
       return (long long)(i_base + mi * 32 + rr0 + RSTEP * s) * a.ldx + j_base + cc;
     };
-    u32x4_t hv[2][RUNS], lv[2][RUNS];
+    u32x4_t hv[2][RUNS];
+    u32x2_t lv[2][RUNS];
     auto load = [&](auto mi, auto b) __attribute__((always_inline)) {
       static_for<RUNS>([&](auto s) {
         const long long o = offset(decltype(mi)::value, s);
         hv[decltype(b)::value][s] = ldx(reinterpret_cast<const u32x4_t*>(Xh + o));
-        lv[decltype(b)::value][s] = ldx(reinterpret_cast<const u32x4_t*>(Xl + o));
+        lv[decltype(b)::value][s] = ldx(reinterpret_cast<const u32x2_t*>(Xl + o));
       });
     };
     load(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
@@ -749,11 +751,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
         if constexpr (FINAL) {
           float x[8];
           static_for<4>([&](auto w) {
-            const unsigned hw = hv[b][s][(int)w], lw = lv[b][s][(int)w];
+            const unsigned hw = hv[b][s][(int)w], lw = lv[b][s][(int)w / 2];
             static_for<2>([&](auto h) {
               constexpr int e = 2 * w + h;
-              const float xe = __uint_as_float(h ? hw & 0xffff0000u : hw << 16) +
-                               __uint_as_float(h ? lw & 0xffff0000u : lw << 16);
+              const float xe =
+                  lo8_x(__uint_as_float(h ? hw & 0xffff0000u : hw << 16), lo8_byte(lw, e % 4));
               x[e] = scl * (a.a * xe + (e < 4 ? p0[e & 3] : p1[e & 3]));
             });
           });
@@ -807,30 +809,29 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
             }
           }
         } else {
-        u32x4_t ho, lo;
+        u32x4_t ho;
+        u32x2_t lo = {0u, 0u};
         [[maybe_unused]] float ss = 0.f;
         static_for<4>([&](auto w) {
-          const unsigned hw = hv[b][s][(int)w], lw = lv[b][s][(int)w];
-          unsigned short hb[2], lb[2];
+          const unsigned hw = hv[b][s][(int)w], lw = lv[b][s][(int)w / 2];
+          unsigned short hb[2];
           static_for<2>([&](auto h) {
             constexpr int e = 2 * w + h;
-            const float x = __uint_as_float(h ? hw & 0xffff0000u : hw << 16) +
-                            __uint_as_float(h ? lw & 0xffff0000u : lw << 16);
+            const float x =
+                lo8_x(__uint_as_float(h ? hw & 0xffff0000u : hw << 16), lo8_byte(lw, e % 4));
             const float accv = e < 4 ? p0[e & 3] : p1[e & 3];
             const float xn = scl * (a.a * x + accv);
             if constexpr (ROWS) ss = fmaf(xn, xn, ss);
-            bf16_t vh, vl;
-            split_bf16(xn, vh, vl);
+            const bf16_t vh = from_f32<bf16_t>(xn);
             hb[h] = __builtin_bit_cast(unsigned short, vh);
-            lb[h] = __builtin_bit_cast(unsigned short, vl);
+            lo[e / 4] |= lo8_of(xn, to_f32(vh)) << (8 * (e % 4));
           });
           ho[(int)w] = (unsigned)hb[0] | ((unsigned)hb[1] << 16);
-          lo[(int)w] = (unsigned)lb[0] | ((unsigned)lb[1] << 16);
         });
         const long long o = offset(mi, s);
         // lo is updated in place: only this block reads X[i][j]'s lo
         stx(ho, reinterpret_cast<u32x4_t*>(Xh_next + o));
-        stx(lo, reinterpret_cast<u32x4_t*>(Xl + o));
+        stx(lo, reinterpret_cast<u32x2_t*>(Xl + o));
         if constexpr (ROWS) {
           // the row's sum over the wave's 64 columns, from the 8 lanes of
           // its runs in a fixed butterfly order (all lanes are active here)
@@ -870,7 +871,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
         if constexpr (EPI == EPI_POLY_LO) ein[nn][e] += to_f32(Alo[(long long)i * a.ldc + j]);
         if constexpr (UPD || FINAL) {
           const long long o = (long long)i * a.ldx + j;
-          if constexpr (HILO) ein[nn][e] = to_f32(Xh[o]) + to_f32(Xl[o]);
+          if constexpr (HILO) ein[nn][e] = lo8_x(to_f32(Xh[o]), (int)(signed char)Xl[o]);
           else ein[nn][e] = Xf[o];
         }
         if constexpr (FIN_W) {
@@ -907,10 +908,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmLaunch launch)
             const long long o = (long long)i * a.ldx + j;
             if constexpr (HILO) {
               // lo is updated in place: only this block reads X[i][j]'s lo
-              bf16_t hi, lo;
-              split_bf16(v[t], hi, lo);
+              const bf16_t hi = from_f32<bf16_t>(v[t]);
               Xh_next[o] = hi;
-              Xl[o] = lo;
+              Xl[o] = (unsigned char)lo8_of(v[t], to_f32(hi));
             } else {
               Xf[o] = v[t];
             }

@@ -35,9 +35,11 @@ enum Final { FINAL_NONE = 0, FINAL_OUT = 1, FINAL_WEIGHTS = 2 };
 // Inputs of the prep kernel: momentum (step) or plain input (orthogonalize),
 // Frobenius partial sums, and the oriented, zero-padded X_0 copies.
 // X state between Newton-Schulz steps, oriented M x N per matrix:
-//   bf16 compute: X = hi + lo, two bf16 planes (hi is also the MFMA operand;
-//                 it is double-buffered because the update reads all of hi
-//                 as its second operand while writing the next hi);
+//   bf16 compute: X = hi + lo, a bf16 plane hi and a plane lo of one signed
+//                 byte per element, x - hi in 1/256 of hi's bf16 spacing
+//                 (lo8_of, 16 significant bits in all); hi is also the MFMA
+//                 operand and is double-buffered, because the update reads all
+//                 of hi as its second operand while writing the next hi;
 //   fp32 compute: X in fp32, plus X^T (N x M) as the update's operand.
 struct PrepArgs {
   int m, n, M, N;          // oriented shape and its padded size
@@ -48,7 +50,7 @@ struct PrepArgs {
   long long s_in;
   float mu;
   long long sX;            // per-matrix stride of the M x N planes
-  void* Xh; void* Xl;      // bf16: hi, lo of X_0
+  void* Xh; void* Xl;      // bf16: hi, lo (bytes) of X_0
   float* Xf;               // fp32: X_0
   void* XT; long long sXT; // fp32: X_0^T, N x M
   float* partials;         // [matrix][tile] sum of u^2

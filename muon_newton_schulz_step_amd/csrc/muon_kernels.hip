@@ -37,7 +37,8 @@ namespace muon {
 // One 64x64 tile of the oriented, padded M x N space per block.  Reads the
 // original matrix coalesced along its rows; outputs that share the original
 // layout are written directly, the others through a transposing LDS tile.
-//   CT = bf16: X_0 as its hi and lo planes (M x N);
+//   CT = bf16: X_0 as its hi plane (bf16) and its lo plane (one byte per
+//              element, lo8_of), M x N each;
 //   CT = fp32: X_0 (M x N) and X_0^T (N x M).
 template <typename GT, typename CT, bool MOM, bool STRM>
 __global__ __launch_bounds__(256) void prep_kernel(PrepLaunch launch) {
@@ -66,22 +67,27 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepLaunch launch) {
     g = static_cast<const GT*>(a.in) + (long long)mat * a.s_in;
   }
   bf16_t* Xh = nullptr;
-  bf16_t* Xl = nullptr;
+  unsigned char* Xl = nullptr;
   float* Xf = nullptr;
   float* XT = nullptr;
   if constexpr (HILO) {
     Xh = static_cast<bf16_t*>(a.Xh) + (long long)mat * a.sX;
-    Xl = static_cast<bf16_t*>(a.Xl) + (long long)mat * a.sX;
+    Xl = static_cast<unsigned char*>(a.Xl) + (long long)mat * a.sX;
   } else {
     Xf = a.Xf + (long long)mat * a.sX;
     XT = static_cast<float*>(a.XT) + (long long)mat * a.sXT;
   }
-  auto put_x = [&](long long o, float u) {  // X[oi][oj] at offset o
+  // X[oi][oj] at offset o.  Every lane of the wave takes part, lane l at
+  // o0 + l for one row run of 64 (o0 a multiple of 64): the lo bytes of 4
+  // neighbouring lanes go out as one 4-byte store.
+  auto put_x = [&](long long o, float u) {
     if constexpr (HILO) {
-      bf16_t hi, lo;
-      split_bf16(u, hi, lo);
+      const bf16_t hi = from_f32<bf16_t>(u);
       stx(hi, Xh + o);
-      stx(lo, Xl + o);
+      const unsigned b = lo8_of(u, to_f32(hi));
+      const unsigned w = b | (__shfl_down(b, 1) << 8) | (__shfl_down(b, 2) << 16) |
+                         (__shfl_down(b, 3) << 24);
+      if ((tid & 3) == 0) stx(w, reinterpret_cast<unsigned*>(Xl + o));
     } else {
       Xf[o] = u;
     }
@@ -163,13 +169,13 @@ __global__ __launch_bounds__(256) void normuon_rows_kernel(NormuonLaunch launch)
   float s = 0.f;
   if constexpr (HILO) {
     const bf16_t* h = static_cast<const bf16_t*>(a.Xh) + row;
-    const bf16_t* l = static_cast<const bf16_t*>(a.Xl) + row;
+    const unsigned char* l = static_cast<const unsigned char*>(a.Xl) + row;
     for (int j = 8 * tid; j < a.N; j += 8 * 256) {
       const bf16x8_t hv = *reinterpret_cast<const bf16x8_t*>(h + j);
-      const bf16x8_t lv = *reinterpret_cast<const bf16x8_t*>(l + j);
+      const u32x2_t lv = *reinterpret_cast<const u32x2_t*>(l + j);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float x = to_f32(hv[e]) + to_f32(lv[e]);
+        const float x = lo8_x(to_f32(hv[e]), lo8_byte(lv[e / 4], e % 4));
         s = fmaf(x, x, s);
       }
     }
@@ -237,8 +243,8 @@ __global__ __launch_bounds__(256) void apply_kernel(ApplyLaunch launch) {
     const long long o = base + (long long)oi * a.ldx + oj;
     float x;
     if constexpr (HILO) {
-      x = to_f32(ld_nt(static_cast<const bf16_t*>(a.Xh) + o)) +
-          to_f32(ld_nt(static_cast<const bf16_t*>(a.Xl) + o));
+      x = lo8_x(to_f32(ld_nt(static_cast<const bf16_t*>(a.Xh) + o)),
+                (int)ld_nt(static_cast<const signed char*>(a.Xl) + o));
     } else {
       x = a.Xf[o];
     }

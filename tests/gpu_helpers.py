@@ -12,9 +12,9 @@ BUF_TOL = 1e-6    # momentum buffer, fp32 arithmetic vs fp64
 # bound per oriented shape (m, n) the GPU tests use, each between the maximum
 # over 1000 Gaussian draws of the emulated bf16 path and 1.25 times it
 # (tests/test_bf16_emulation.py recomputes the maxima and checks every entry:
-# 1x1 0.120, 1x5 0.094, 2x8 0.117, 5x5 0.072, 8x16 0.039).  From min dim 64 on
+# 1x1 0.118, 1x5 0.099, 2x8 0.117, 5x5 0.062, 8x16 0.037).  From min dim 64 on
 # the emulated maximum stays below 2e-2 (64x64: 1.8e-2, 128x128: 1.5e-2).
-BF16_SMALL_TOL = {(1, 1): 0.15, (1, 5): 0.11, (2, 8): 0.14, (5, 5): 0.09, (8, 16): 0.048}
+BF16_SMALL_TOL = {(1, 1): 0.14, (1, 5): 0.11, (2, 8): 0.14, (5, 5): 0.075, (8, 16): 0.045}
 SMALL_DIM = 64
 # bf16 path on degenerate inputs (workloads.degenerate_matrix) whose
 # singular vectors are flat: the bf16 rounding of B is then the same in many
@@ -22,9 +22,9 @@ SMALL_DIM = 64
 # the emulated bf16 path stays within 0.8 BF16_TOL on the shapes the GPU test
 # uses (DEGENERATE_SHAPES); otherwise its bound lies between 1.1 and 1.25
 # times the emulated maximum (tests/test_bf16_emulation.py checks both:
-# constant 2.10e-2, duplicated rows 1.91e-2).
+# constant 2.04e-2, duplicated rows 1.73e-2).
 DEGENERATE_SHAPES = ((256, 384), (384, 256), (1024, 3072))
-DEGENERATE_BF16_TOL = {"constant": 2.6e-2, "dup_rows": 2.3e-2}
+DEGENERATE_BF16_TOL = {"constant": 2.5e-2, "dup_rows": 2.1e-2}
 
 
 def degenerate_tol(kind, compute):

@@ -223,11 +223,11 @@ def test_workspace_sizes():
               (12288, 3072), (3072, 12288)] * 28
     ws = mn.step_workspace_bytes(shapes)
     assert ws == lib.muon_orthogonalize_workspace_bytes(56, 3072, 12288, 0)
-    # bf16: X as hi (twice) and lo planes, 2 bytes each, A and B (bf16), A's
-    # residual and the product T of the Q A Q steps (bf16; this group has
-    # N = 4M and M >= 2048), the fp32 norm partials of 64 x 64 tiles and the
-    # per-matrix 1/norm
-    need = 56 * (3 * 3072 * 12288 * 2 + 4 * 3072 * 3072 * 2
+    # bf16: X as hi (twice, 2 bytes each) and lo (1 byte) planes, A and B
+    # (bf16), A's residual and the product T of the Q A Q steps (bf16; this
+    # group has N = 4M and M >= 2048), the fp32 norm partials of 64 x 64 tiles
+    # and the per-matrix 1/norm
+    need = 56 * (5 * 3072 * 12288 + 4 * 3072 * 3072 * 2
                  + (3072 // 64) * (12288 // 64) * 4 + 4)
     assert need <= ws < need + 8 * 256
 
@@ -290,9 +290,9 @@ def static_call(n=2, rows=(8, 16), cols=(16, 8), params=None, grads=None, bufs=N
     (dict(param_dtype=0), mn.MUON_ERR_UNSUPPORTED),
     (dict(mu=float("nan")), mn.MUON_ERR_INVALID_ARG),
     (dict(n_steps=65, coeffs=Q * 13), mn.MUON_ERR_INVALID_ARG),
-    # one 3072 x 12288 matrix needs more than the fixed scratch area: refused
+    # one 4096 x 16384 matrix needs more than the fixed scratch area: refused
     # before anything touches the GPU
-    (dict(n=1, rows=(3072,), cols=(12288,), params=[1 << 40], grads=[2 << 40],
+    (dict(n=1, rows=(4096,), cols=(16384,), params=[1 << 40], grads=[2 << 40],
           bufs=[3 << 40]), mn.MUON_ERR_WORKSPACE),
 ])
 def test_step_static_rejects_before_enqueue(kw, expect):
@@ -306,11 +306,11 @@ def test_static_scratch_size_matches_header():
     lib = mn.lib()
     # the limit applies to the largest chunk (the static entry point runs its
     # chunks one after the other): the 8-layer d768 GPT set fits, one
-    # (3072, 12288) matrix does not
+    # (4096, 16384) matrix does not
     largest = max(mn.orthogonalize_workspace_bytes(32, 768, 768),
                   mn.orthogonalize_workspace_bytes(16, 768, 3072))
     assert 0 < largest <= _lib.MUON_STATIC_SCRATCH_BYTES
-    big = lib.muon_step_workspace_bytes(1, _lib.int_array([3072]), _lib.int_array([12288]), 0)
+    big = lib.muon_step_workspace_bytes(1, _lib.int_array([4096]), _lib.int_array([16384]), 0)
     assert big > _lib.MUON_STATIC_SCRATCH_BYTES
 
 

@@ -3,13 +3,14 @@ and to check two design choices; it is never the parity reference (that is
 the fp64 oracle).
 
 The emulated arithmetic follows the library's bf16 path step by step:
-  * X_0 is the fp32 input u carried as two bf16 planes, hi = bf16(u) and
-    lo = bf16(u - hi); the Frobenius norm is folded in as 1/(||u|| + eps)
-    (squared into the first Gram matrix, once into the first update);
+  * X_0 is the fp32 input u carried as hi = bf16(u) and a signed byte lo,
+    u - hi in 1/256 of hi's bf16 spacing (lo8 below); the Frobenius norm is
+    folded in as 1/(||u|| + eps) (squared into the first Gram matrix, once
+    into the first update);
   * every product takes bf16 operands (X's hi plane, A, B, or T), multiplies
     exactly and accumulates in fp32;
   * A and B are stored as bf16 (round to nearest even), X between steps as
-    hi + lo of the fp32 update a X + B X;
+    hi + lo of the fp32 update a X + B X, in the same 3-byte form;
   * in Q A Q Gram steps (wide groups with N >= 4M, M >= 2048 on the GPU), A
     is formed from the previous step as T = a' (A + A_lo) + B A, then
     A = a' T + T B, with A_lo A's bf16 residual.
@@ -42,11 +43,27 @@ def f32(x):
     return np.asarray(x, np.float64).astype(np.float32)
 
 
-def emulate(u, coeffs, xstate="hilo", qaq_steps=(), exact=False):
+def lo8(x):
+    """x as (hi, lo) with hi = bf16(x) and lo = q * ulp(hi) / 256, q the
+    signed byte round((x - hi) * 256 / ulp(hi)) clamped to [-128, 127];
+    ulp(hi) is the bf16 spacing of hi's binade (the smallest normal one's for
+    zero and subnormal hi).  Both returned as fp32 values."""
+    x = f32(x)
+    hi = bf16(x)
+    e = np.maximum((hi.view(np.uint32) >> 23) & 0xFF, 1).astype(np.int64)
+    unit = np.ldexp(1.0, e - 142)                      # ulp(hi) / 256
+    with np.errstate(invalid="ignore"):
+        q = np.clip(np.rint((x.astype(np.float64) - hi) / unit), -128, 127)
+    q = np.where(np.isfinite(hi) & (e < 254), q, 0.0)
+    return hi, f32(q * unit)
+
+
+def emulate(u, coeffs, xstate="lo8", qaq_steps=(), exact=False):
     """O for the fp32 input u as the bf16 path computes it.
 
-    xstate "hilo": X kept as hi + lo between steps (the library); "bf16": X
-    kept as bf16 alone (the rejected design).  qaq_steps: steps whose Gram
+    xstate "lo8": X kept as hi + a one-byte lo between steps (the library);
+    "hilo": hi + lo as two bf16 values (the same 16 bits in 4 bytes); "bf16":
+    X kept as bf16 alone (the rejected design).  qaq_steps: steps whose Gram
     matrix is formed as Q A Q (never step 0 or the last step).  exact: no
     rounding at all, fp64 throughout (must equal the oracle)."""
     rnd = (lambda x: np.asarray(x, np.float64)) if exact else bf16
@@ -62,8 +79,15 @@ def emulate(u, coeffs, xstate="hilo", qaq_steps=(), exact=False):
     s = float(np.sum(np.asarray(u, np.float64) ** 2))
     inv = 1.0 / (np.sqrt(s) + oracle.DEFAULT_EPS)
     inv = float(inv) if exact else np.float32(inv)
-    hi = rnd(u)
-    lo = rnd(fl(u - hi)) if xstate == "hilo" else np.zeros_like(u)
+    def split(x):
+        if exact:
+            return x, np.zeros_like(x)
+        if xstate == "lo8":
+            return lo8(x)
+        hi = rnd(x)
+        return hi, (rnd(fl(x - hi)) if xstate == "hilo" else np.zeros_like(x))
+
+    hi, lo = split(u)
     A = B = Alo = None
     n_steps = len(coeffs)
     for k, (a, b, c) in enumerate(coeffs):
@@ -85,8 +109,7 @@ def emulate(u, coeffs, xstate="hilo", qaq_steps=(), exact=False):
         if k == n_steps - 1:
             out = np.asarray(x, np.float64)
             return out.T if tall else out
-        hi = rnd(x)
-        lo = rnd(fl(x - hi)) if xstate == "hilo" else np.zeros_like(x)
+        hi, lo = split(x)
 
 
 def emulated_errors(shape, draws, seed):
@@ -175,12 +198,40 @@ def _inputs(kind, m, n, seed):
 @pytest.mark.parametrize("kind", ["lowrank", "logspec"])
 def test_x_state_needs_more_than_bf16(kind):
     """X carried between steps as bf16 alone misses the 2e-2 bar on
-    structured inputs; as hi + lo (16 significant bits) it stays far inside."""
+    structured inputs; with 16 significant bits it stays far inside, and the
+    one-byte lo gives the error of a second bf16 value within 3%."""
     g = _inputs(kind, 256, 1024, 11)
     ref = oracle.orthogonalize(g.astype(np.float64), Q5)
-    e_hilo = oracle.relative_frobenius_error(emulate(g, Q5), ref)
+    e_lo8 = oracle.relative_frobenius_error(emulate(g, Q5), ref)
+    e_hilo = oracle.relative_frobenius_error(emulate(g, Q5, xstate="hilo"), ref)
     e_bf16 = oracle.relative_frobenius_error(emulate(g, Q5, xstate="bf16"), ref)
-    assert e_hilo <= 0.5 * BF16_TOL and e_bf16 > BF16_TOL, (e_hilo, e_bf16)
+    assert e_lo8 <= 0.5 * BF16_TOL and e_bf16 > BF16_TOL, (e_lo8, e_bf16)
+    assert abs(e_lo8 / e_hilo - 1.0) <= 0.03, (e_lo8, e_hilo)
+
+
+def test_lo8_holds_sixteen_bits():
+    """hi + lo of the one-byte form is within 1/512 of hi's bf16 spacing of
+    x (2^-16 relative) from 2^-140 to 2^126, except where x - hi is within
+    1/512 of that spacing below +1/2 of it: there q = 128 is clamped to 127
+    and the error is at most 1/256.  Zero stays zero; a non-finite hi keeps
+    lo = 0."""
+    rng = np.random.default_rng(5)
+    mant = rng.uniform(1.0, 2.0, 4000) * rng.choice([-1.0, 1.0], 4000)
+    x = f32(mant * np.exp2(rng.integers(-140, 127, 4000)))
+    hi, lo = lo8(x)
+    e = np.maximum((hi.view(np.uint32) >> 23) & 0xFF, 1).astype(np.int64)
+    ulp = np.exp2((e - 134).astype(np.float64))
+    d = x.astype(np.float64) - hi
+    err = np.abs(d - lo)
+    clamped = d > ulp * (127.5 / 256)
+    assert 0 < clamped.sum() < 0.01 * x.size
+    assert np.all(err[~clamped] <= ulp[~clamped] / 512)
+    assert np.all(err[clamped] <= ulp[clamped] / 256)
+    assert np.all(np.abs(d) <= ulp / 2)
+    z_hi, z_lo = lo8(np.zeros(3, np.float32))
+    assert not z_hi.any() and not z_lo.any()
+    s_hi, s_lo = lo8(np.array([np.inf, -np.inf, np.nan], np.float32))
+    assert not s_lo.any() and np.isinf(s_hi[:2]).all() and np.isnan(s_hi[2])
 
 
 @pytest.mark.parametrize("kind", ["lowrank", "logspec"])

@@ -77,9 +77,9 @@ def test_static_scratch_two_calls_match_workspace_step(compute):
 
 def test_static_scratch_refuses_too_large_step():
     announce("static scratch: too large")
-    p = torch.zeros(3072, 12288, device=DEV)
-    g = torch.ones(3072, 12288, dtype=torch.bfloat16, device=DEV)
-    b = torch.zeros(3072, 12288, device=DEV)
+    p = torch.zeros(4096, 16384, device=DEV)
+    g = torch.ones(4096, 16384, dtype=torch.bfloat16, device=DEV)
+    b = torch.zeros(4096, 16384, device=DEV)
     with pytest.raises(mn.MuonError, match="WORKSPACE"):
         mn.step_static([p], [g], [b], mu=0.95, lr=0.02)
     torch.cuda.synchronize()
