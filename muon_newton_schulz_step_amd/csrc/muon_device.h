@@ -51,36 +51,28 @@ __device__ __forceinline__ void split_bf16(float x, bf16_t& hi, bf16_t& lo) {
 }
 
 // The X state of the bf16 path between Newton-Schulz steps: hi = bf16(x) and
-// one signed byte q, x - hi in units of 1/256 of hi's bf16 spacing (ulp(hi):
-// 2^(e - 134) for hi's exponent field e, the smallest normal binade's for a
-// zero or subnormal hi):
-//   q = round((x - hi) * 256 / ulp(hi)), clamped to [-128, 127],
-//   x = hi + q * ulp(hi) / 256 to within ulp(hi) / 512,
+// one signed byte q, x - hi in units of 1/256 of hi's bf16 spacing.  With
+// hi = f * 2^e, f in [0.5, 1) (frexp; e = 0 for zero and non-finite hi), the
+// spacing is 2^(e - 8) and the unit 2^(e - 16):
+//   q = round((x - hi) * 2^(16 - e)), clamped to [-128, 127],
+//   x = hi + q * 2^(e - 16) to within 2^(e - 17), ulp/512,
 // 16 significant bits, as hi + bf16(x - hi) would hold, in 3 bytes instead
-// of 4.  |x - hi| <= ulp(hi) / 2, so only q = 128 is clamped (x - hi within
-// ulp/512 below +ulp/2, about one element in 512; error up to ulp/256).  A
-// non-finite hi (or |hi| >= 2^127) keeps q = 0; x comes back as NaN where hi
-// is not finite (0 * inf), as hi + bf16(x - hi) did.
-__device__ __forceinline__ unsigned lo8_exp(float hi) {
-  const unsigned e = (__float_as_uint(hi) >> 23) & 0xffu;
-  return e < 1u ? 1u : e;
-}
-// ulp(hi) / 256 = 2^(e - 127) * 2^-15
-__device__ __forceinline__ float lo8_unit(float hi) {
-  return __uint_as_float(lo8_exp(hi) << 23) * 0x1p-15f;
-}
-// q of x (hi = bf16(x)), as the byte's bit pattern in bits 0..7
+// of 4.  |x - hi| <= ulp/2, so only q = 128 is clamped (x - hi within ulp/512
+// below +ulp/2, about one element in 512; error up to ulp/256).  hi = 0 (|x|
+// below the bf16 subnormals) keeps q = 0; a non-finite hi keeps q = 0 and
+// comes back as itself.  For a subnormal hi (|x| < 2^-126, outside the
+// library's input range) the unit is finer than the spacing and q
+// saturates: x keeps hi's absolute accuracy, 2^-134.  Both directions are a
+// frexp and an ldexp (v_frexp_exp_i32_f32, v_ldexp_f32).
 __device__ __forceinline__ unsigned lo8_of(float x, float hi) {
-  const unsigned e = lo8_exp(hi);
-  // (x - hi) / 2^(e - 142) = (x - hi) * 2^(127 - e) * 2^15, both factors exact
-  const float inv = e < 254u ? __uint_as_float((254u - e) << 23) : 0.f;
-  const float q = __builtin_rintf((x - hi) * inv * 32768.f);
+  const int e = __builtin_amdgcn_frexp_expf(hi);
+  const float q = __builtin_rintf(__builtin_amdgcn_ldexpf(x - hi, 16 - e));
   const int qi = (int)__builtin_fminf(__builtin_fmaxf(q, -128.f), 127.f);
   return (unsigned)qi & 0xffu;
 }
 // x from hi and the signed byte q
 __device__ __forceinline__ float lo8_x(float hi, int q) {
-  return __builtin_fmaf((float)q, lo8_unit(hi), hi);
+  return hi + __builtin_amdgcn_ldexpf((float)q, __builtin_amdgcn_frexp_expf(hi) - 16);
 }
 // the signed byte b (0..3) of a packed word
 __device__ __forceinline__ int lo8_byte(unsigned w, int b) {

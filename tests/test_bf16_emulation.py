@@ -44,17 +44,17 @@ def f32(x):
 
 
 def lo8(x):
-    """x as (hi, lo) with hi = bf16(x) and lo = q * ulp(hi) / 256, q the
-    signed byte round((x - hi) * 256 / ulp(hi)) clamped to [-128, 127];
-    ulp(hi) is the bf16 spacing of hi's binade (the smallest normal one's for
-    zero and subnormal hi).  Both returned as fp32 values."""
+    """x as (hi, lo) with hi = bf16(x) and lo = q * 2^(e - 16), q the signed
+    byte round((x - hi) * 2^(16 - e)) clamped to [-128, 127], where hi =
+    f * 2^e with f in [0.5, 1) (frexp; e = 0 for zero and non-finite hi), so
+    2^(e - 16) is 1/256 of hi's bf16 spacing.  Both returned as fp32 values."""
     x = f32(x)
     hi = bf16(x)
-    e = np.maximum((hi.view(np.uint32) >> 23) & 0xFF, 1).astype(np.int64)
-    unit = np.ldexp(1.0, e - 142)                      # ulp(hi) / 256
+    _, e = np.frexp(np.where(np.isfinite(hi), hi, 0.0).astype(np.float64))
+    unit = np.ldexp(1.0, e.astype(np.int64) - 16)
     with np.errstate(invalid="ignore"):
         q = np.clip(np.rint((x.astype(np.float64) - hi) / unit), -128, 127)
-    q = np.where(np.isfinite(hi) & (e < 254), q, 0.0)
+    q = np.where(np.isfinite(hi), q, 0.0)
     return hi, f32(q * unit)
 
 
@@ -211,15 +211,15 @@ def test_x_state_needs_more_than_bf16(kind):
 
 def test_lo8_holds_sixteen_bits():
     """hi + lo of the one-byte form is within 1/512 of hi's bf16 spacing of
-    x (2^-16 relative) from 2^-140 to 2^126, except where x - hi is within
-    1/512 of that spacing below +1/2 of it: there q = 128 is clamped to 127
-    and the error is at most 1/256.  Zero stays zero; a non-finite hi keeps
-    lo = 0."""
+    x (2^-16 relative) over fp32's normal range, 2^-126 to 2^126, except where
+    x - hi is within 1/512 of that spacing below +1/2 of it: there q = 128 is
+    clamped to 127 and the error is at most 1/256.  Zero stays zero; a
+    non-finite hi keeps lo = 0."""
     rng = np.random.default_rng(5)
     mant = rng.uniform(1.0, 2.0, 4000) * rng.choice([-1.0, 1.0], 4000)
-    x = f32(mant * np.exp2(rng.integers(-140, 127, 4000)))
+    x = f32(mant * np.exp2(rng.integers(-126, 127, 4000)))
     hi, lo = lo8(x)
-    e = np.maximum((hi.view(np.uint32) >> 23) & 0xFF, 1).astype(np.int64)
+    e = ((hi.view(np.uint32) >> 23) & 0xFF).astype(np.int64)
     ulp = np.exp2((e - 134).astype(np.float64))
     d = x.astype(np.float64) - hi
     err = np.abs(d - lo)
