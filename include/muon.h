@@ -115,8 +115,9 @@ int muon_plan_groups(int n, const int* rows, const int* cols, int* group_of,
  *   coeffs        host, n_steps rows (copied during the call).
  *   eps           >= 0, finite (the step's default is 1e-7).
  *   compute       MUON_BF16: bf16 MFMA operands with fp32 accumulation; X is
- *                 carried between steps as two bf16 values (hi + lo, 16
- *                 significant bits) for the a*X term; for matrices whose
+ *                 carried between steps as hi = bf16(x) and one signed byte,
+ *                 x - hi in 1/256 of hi's bf16 spacing (16 significant bits,
+ *                 3 bytes) for the a*X term; for matrices whose
  *                 padded shape has n >= 4m and m >= 2048, the A of steps 1
  *                 and 3 is formed as Q A Q from the step before (Q = aI + B;
  *                 equal to X X^T in exact arithmetic).  MUON_FP32: fp32
