@@ -180,6 +180,32 @@ def test_magnitude_range(compute):
         assert err <= tol(compute, (64, 192)), (k, err)
 
 
+@pytest.mark.parametrize("shape", [(200, 520), (520, 200)], ids=["wide", "tall"])
+@pytest.mark.parametrize("n_steps", [1, 3])
+def test_x_state_holds_sixteen_bits(shape, n_steps):
+    """With the coefficients (1, 0, 0) every Newton-Schulz step gives X back
+    (a X + (0 A + 0 A^2) X), so the bf16 path's output is the normalised
+    fp32 input as carried by its X state: prep encodes it once, every further
+    update re-encodes it, the last one decodes it.  Each encoding keeps 16
+    significant bits (hi = bf16(x) and a signed byte of 1/256 of hi's
+    spacing: relative error at most 2^-16, 2^-15 where the byte saturates),
+    so every element is within n_steps * 2^-15 of the oracle's u / (||u|| +
+    eps), plus fp32 rounding.  A state that kept hi alone would be off by up
+    to 2^-9."""
+    announce("X state precision", shape, n_steps)
+    x = wl.gaussian_matrix(*shape, seed=23, device=DEV)
+    ident = [(1.0, 0.0, 0.0)] * n_steps
+    o = to64(mn.orthogonalize(x, ident, compute="bf16", out_dtype=torch.float32))
+    ref = oracle.orthogonalize(to64(x), ident)
+    assert np.allclose(ref, normalise(to64(x)), rtol=1e-15, atol=0)
+    rel = np.abs(o - ref) / np.abs(ref)
+    print("max relative error per element %.3e" % rel.max())
+    assert rel.max() <= n_steps * 2.0 ** -15 + 8 * 2.0 ** -24
+    # the low part carries information: hi alone is much further off
+    hi_only = to64(torch.from_numpy(ref).float().to(torch.bfloat16))
+    assert (np.abs(hi_only - ref) / np.abs(ref)).max() > 16 * rel.max()
+
+
 def test_permutation_invariance():
     announce("permutation invariance")
     x = wl.gaussian_matrix(200, 330, seed=10, device=DEV)
