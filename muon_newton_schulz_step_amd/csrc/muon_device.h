@@ -52,27 +52,30 @@ __device__ __forceinline__ void split_bf16(float x, bf16_t& hi, bf16_t& lo) {
 
 // The X state of the bf16 path between Newton-Schulz steps: hi = bf16(x) and
 // one signed byte q, x - hi in units of 1/256 of hi's bf16 spacing.  With
-// hi = f * 2^e, f in [0.5, 1) (frexp; e = 0 for zero and non-finite hi), the
-// spacing is 2^(e - 8) and the unit 2^(e - 16):
-//   q = round((x - hi) * 2^(16 - e)), clamped to [-128, 127],
+// hi = f * 2^e, f in [0.5, 1) (frexp), the spacing is 2^(e - 8) and the unit
+// 2^(e - 16):
+//   q = round((x - hi) * 2^(16 - e)) (to nearest even), clamped to [-128, 127],
 //   x = hi + q * 2^(e - 16) to within 2^(e - 17), ulp/512,
 // 16 significant bits, as hi + bf16(x - hi) would hold, in 3 bytes instead
 // of 4.  |x - hi| <= ulp/2, so only q = 128 is clamped (x - hi within ulp/512
-// below +ulp/2, about one element in 512; error up to ulp/256).  hi = 0 (|x|
-// below the bf16 subnormals) keeps q = 0; a non-finite hi keeps q = 0 and
-// comes back as itself.  For a subnormal hi (|x| < 2^-126, outside the
-// library's input range) the unit is finer than the spacing and q
-// saturates: x keeps hi's absolute accuracy, 2^-134.  Both directions are a
-// frexp and an ldexp (v_frexp_exp_i32_f32, v_ldexp_f32).
+// below +ulp/2, about one element in 512; error up to ulp/256).  The decode
+// takes the unit from hi's exponent bits, so a zero or subnormal hi (|x| <
+// 2^-126, outside the library's input range) comes back as hi, and a
+// non-finite x as NaN (as hi + bf16(x - hi) did).  The encode is a frexp, an
+// ldexp, a clamp and an add; the decode a mask, a multiply and an fma.
 __device__ __forceinline__ unsigned lo8_of(float x, float hi) {
   const int e = __builtin_amdgcn_frexp_expf(hi);
-  const float q = __builtin_rintf(__builtin_amdgcn_ldexpf(x - hi, 16 - e));
-  const int qi = (int)__builtin_fminf(__builtin_fmaxf(q, -128.f), 127.f);
-  return (unsigned)qi & 0xffu;
+  const float q = __builtin_fminf(
+      __builtin_fmaxf(__builtin_amdgcn_ldexpf(x - hi, 16 - e), -128.f), 127.f);
+  // round to nearest even by adding 1.5 * 2^23: the sum's low mantissa bits
+  // are the rounded integer, its low byte q's two's complement byte
+  return __float_as_uint(q + 0x1.8p23f) & 0xffu;
 }
-// x from hi and the signed byte q
+// x from hi and the signed byte q: the unit 2^(e - 16) is hi's exponent
+// bits times 2^-15 (0 for a zero or subnormal hi, whose q is then ignored)
 __device__ __forceinline__ float lo8_x(float hi, int q) {
-  return hi + __builtin_amdgcn_ldexpf((float)q, __builtin_amdgcn_frexp_expf(hi) - 16);
+  return __builtin_fmaf((float)q, __uint_as_float(__float_as_uint(hi) & 0x7f800000u) * 0x1p-15f,
+                        hi);
 }
 // the signed byte b (0..3) of a packed word
 __device__ __forceinline__ int lo8_byte(unsigned w, int b) {
